@@ -1,0 +1,273 @@
+"""Benchmark of the MoE layer forward on one MI355X.
+
+One step = one ``moe_forward`` call (router, top-k gating, permutation, both
+expert GEMMs, combine) over one batch of synthetic tokens already resident in
+HBM.  The default workload is the Qwen3-30B-A3B-shaped decode step (T=64,
+d=2048, E=128, k=8, F=768, bf16), which streams most expert weights from HBM
+("Serve MoE models with expert parallelism", section "Start with one device if
+the model fits": a batch of many tokens touches many experts, so a decode step
+reads more of the weights as the batch grows).  ``--config`` selects the other
+workloads (prefill, mixtral, dsv3_rank, tiny).
+
+Weights are held in several copies in HBM and the steps rotate through them,
+so that no step finds another step's weights in the 256 MB Infinity Cache.
+
+Prints one JSON line: whole-layer tokens/s, plus a roofline object for the
+dominant kernel (the gate/up grouped GEMM) timed with HIP events on the
+library's stream, and a CPU baseline of the float64 oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from mixture_experts_layer_15_amd import binding as B  # noqa: E402
+from mixture_experts_layer_15_amd import synth  # noqa: E402
+
+METRIC = "MoE-layer tokens/s; % of MFMA peak (prefill) or HBM GB/s peak (decode)"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # dense fp8 MFMA
+PEAK_FP32_TFLOPS = 157.3       # fp32 vector / matrix
+ACT_BYTES = {"f32": 4, "bf16": 2}
+W_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
+
+# Dominant-kernel names as they appear in a rocprofv3 kernel trace.
+KERNEL_NAMES = {
+    "gate_up": "grouped_gemm_kernel<{mb}, {wm}, {nb}, {wn}, true, {fp8}, {mnb}>",
+}
+
+
+def expert_bytes(d: int, F: int, wfmt: str, n_experts: int, with_scales: bool = True) -> int:
+    """Weight bytes of n whole SwiGLU experts: 3 d F parameters each, times the
+    bytes per parameter ("Expert Parallelism for MoE Models", section "Memory
+    Sizing Equations": expert memory = experts x parameters per expert x bytes
+    per parameter), plus the FP8 block scales."""
+    b = n_experts * 3 * d * F * W_BYTES[wfmt]
+    if wfmt == "fp8" and with_scales:
+        b += n_experts * 3 * (d // 128) * (F // 128) * 4
+    return b
+
+
+def algorithmic(wl: synth.Workload, counts: np.ndarray) -> dict:
+    """Algorithmic FLOPs and HBM bytes of one layer step and of the gate/up GEMM."""
+    d, F, E, T, k = wl.d, wl.F, wl.E, wl.T, wl.k
+    ab, wb = ACT_BYTES[wl.act], W_BYTES[wl.weight]
+    N = int(counts.sum())
+    touched = int((counts > 0).sum())
+    tokens_read = T  # every token row is read once (all of them are routed)
+    router = 2 * T * d * E
+    layer_flop = router + 6 * N * d * F
+    layer_bytes = (expert_bytes(d, F, wl.weight, touched) + d * E * ab + T * E * 4
+                   + tokens_read * d * ab + T * d * ab)
+    gu_flop = 4 * N * d * F
+    gu_scales = 2 * (d // 128) * (F // 128) * 4 if wl.weight == "fp8" else 0
+    gu_bytes = touched * (2 * d * F * wb + gu_scales) + tokens_read * d * ab + N * F * ab
+    return dict(N=N, touched=touched, layer_flop=layer_flop, layer_bytes=layer_bytes,
+                gu_flop=gu_flop, gu_bytes=gu_bytes, gu_unit_bytes=2 * d * F * wb + gu_scales)
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (for the events moe_forward records on its stream)."""
+
+    def __init__(self, n: int):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(h)) == 0
+            self.arr[i] = h.value
+
+    def sync(self, i: int) -> None:
+        assert self.hip.hipEventSynchronize(ctypes.c_void_p(self.arr[i])) == 0
+
+    def ms(self, a: int, b: int) -> float:
+        out = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(out), ctypes.c_void_p(self.arr[a]),
+                                            ctypes.c_void_p(self.arr[b])) == 0
+        return float(out.value)
+
+
+def cpu_baseline(pr: synth.Problem, logits: torch.Tensor, budget_s: float) -> dict:
+    """The float64 oracle, as it stands, on whole steps of the same workload
+    (or on a token sample when one step would exceed the budget)."""
+    from oracle import moe_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    wl = pr.wl
+    raw = {n: synth.raw(getattr(pr, n)) for n in ("x", "w_router", "w_gate", "w_up", "w_down",
+                                                  "s_gate", "s_up", "s_down")}
+    bias = None if pr.bias is None else pr.bias.numpy()
+    L32 = logits.cpu().numpy()
+    rng = np.random.default_rng(0)
+    # a sample small enough for ~budget_s of work: whole steps when cheap
+    sample = None if wl.T <= 256 else np.sort(rng.choice(wl.T, size=64, replace=False))
+    n_tok, t0, reps = 0, time.perf_counter(), 0
+    while True:
+        x64 = orc.decode_act(raw["x"] if sample is None else raw["x"][sample], wl.act)
+        orc.router_logits(x64, orc.decode_act(raw["w_router"], wl.act), bias)
+        orc.moe_layer_forward(raw["x"], L32, wl.k, raw["w_gate"], raw["w_up"], raw["w_down"],
+                              act_fmt=wl.act, weight_fmt=wl.weight, e0=wl.expert_begin,
+                              E_l=wl.num_local, s_gate=raw["s_gate"], s_up=raw["s_up"],
+                              s_down=raw["s_down"], tokens=sample)
+        n_tok += wl.T if sample is None else len(sample)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 50:
+            break
+    what = (f"{reps} whole step(s) of T={wl.T}" if sample is None else
+            f"{reps} x 64 sampled tokens of T={wl.T} (routing of all T each time)")
+    return {"value": n_tok / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": what, "seconds": round(el, 2),
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--config", default="decode", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--weight-copies", type=int, default=None)
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share of the MoE layer: only --gpus 1 is supported "
+              "(expert-parallel sharding across GPUs is not built).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    wl = synth.WORKLOADS[args.config]
+    steps = args.steps or (200 if wl.regime in ("decode", "tiny") else 50)
+    warmup = args.warmup if args.warmup is not None else 10
+    dev = torch.device("cuda:0")
+    B.load_library()
+    pr = synth.make_problem(wl)
+    p = B.problem(wl.T, wl.d, wl.E, wl.k, wl.F, wl.expert_begin, wl.num_local, wl.act, wl.weight)
+
+    wbytes = expert_bytes(wl.d, wl.F, wl.weight, wl.num_local)
+    copies = args.weight_copies or max(2, min(8, -(-1024 ** 3 // wbytes) + 1))
+    x = pr.x.to(dev)
+    wr = pr.w_router.to(dev)
+    bias = None if pr.bias is None else pr.bias.to(dev)
+    wsets = []
+    for c in range(copies):
+        wsets.append({n: (None if getattr(pr, n) is None else getattr(pr, n).to(dev))
+                      for n in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")})
+    out = torch.empty((wl.T, wl.d), dtype=pr.x.dtype, device=dev)
+    logits = torch.empty((wl.T, wl.E), dtype=torch.float32, device=dev)
+    counts = torch.empty((wl.num_local,), dtype=torch.int32, device=dev)
+    ws = B.workspace(p, B.MOE_CALL_FORWARD, dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i: int, events=None) -> None:
+        w = wsets[i % copies]
+        B.moe_forward(p, x=x, w_router=wr, router_bias=bias, w_gate=w["w_gate"], w_up=w["w_up"],
+                      w_down=w["w_down"], s_gate=w["s_gate"], s_up=w["s_up"], s_down=w["s_down"],
+                      out=out, ws=ws, logits=logits, counts=counts, events=events, stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print(f"[bench] {wl.name}: warmup {warmup} done, timing {steps} steps", file=sys.stderr,
+          flush=True)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / steps
+
+    # Stage times: the same steps again, with HIP events recorded by the library
+    # on its stream at every stage boundary.
+    ev_sets = [HipEvents(B.MOE_FORWARD_EVENTS) for _ in range(steps)]
+    for i in range(steps):
+        step(i, ev_sets[i].arr)
+    torch.cuda.synchronize()
+    names = ["route", "permute", "schedule", "gate_up", "down", "combine"]
+    stage_ms = {n: 0.0 for n in names}
+    layer_ev_ms = 0.0
+    for e in ev_sets:
+        e.sync(6)
+        for s_i, n in enumerate(names):
+            stage_ms[n] += e.ms(s_i, s_i + 1)
+        layer_ev_ms += e.ms(0, 6)
+    stage_ms = {n: v / steps for n, v in stage_ms.items()}
+    layer_ev_ms /= steps
+
+    cnt = counts.cpu().numpy()
+    alg = algorithmic(wl, cnt)
+    t_layer = ms_per_step * 1e-3
+    t_gu = stage_ms["gate_up"] * 1e-3
+    decode = wl.regime in ("decode", "tiny")
+    if decode:
+        achieved = alg["gu_bytes"] / t_gu / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    else:
+        peak = PEAK_FP32_TFLOPS if wl.weight == "f32" else PEAK_BF16_TFLOPS
+        achieved = alg["gu_flop"] / t_gu / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
+        if wl.weight == "fp8":
+            roof["frac_of_fp8_peak"] = round(achieved / PEAK_FP8_TFLOPS, 4)
+    bm, mb, wm = (32, 1, 1) if wl.T * wl.k <= 64 * wl.num_local else (128, 2, 2)
+    nb, wn = (2, 4) if bm == 32 else (4, 2)
+    roof["kernel"] = KERNEL_NAMES["gate_up"].format(
+        mb=mb, wm=wm, nb=nb, wn=wn, fp8=str(wl.weight == "fp8").lower(), mnb=2 if bm == 32 else 1)
+    roof["kernel_ms"] = round(stage_ms["gate_up"], 5)
+    roof["bytes_per_launch"] = alg["gu_bytes"]
+    roof["flop_per_launch"] = alg["gu_flop"]
+
+    result = {
+        "metric": METRIC,
+        "value": round(wl.T / t_layer, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.act if wl.weight != "fp8" else "bf16 (fp8-e4m3 weights)",
+        "data": "synthetic (seeded; random-init weights of the workload's shape)",
+        "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "E": wl.E, "k": wl.k, "F": wl.F,
+                   "local_experts": f"{wl.expert_begin}-{wl.expert_begin + wl.num_local - 1}",
+                   "act": wl.act, "weights": wl.weight, "weight_copies": copies,
+                   "parallelism": "single GPU (all experts local)" if wl.num_local == wl.E
+                   else "one expert-parallel rank's expert block"},
+        "layer": {"tflops": round(alg["layer_flop"] / t_layer / 1e12, 2),
+                  "gbs": round(alg["layer_bytes"] / t_layer / 1e9, 1),
+                  "frac_hbm": round(alg["layer_bytes"] / t_layer / 1e9 / PEAK_HBM_GBS, 4),
+                  "frac_mfma_bf16": round(alg["layer_flop"] / t_layer / 1e12 / PEAK_BF16_TFLOPS, 4),
+                  "kept_slots": alg["N"], "touched_experts": alg["touched"],
+                  "max_over_mean_load": round(float(cnt.max() / max(cnt.mean(), 1e-9)), 2),
+                  "stage_ms": {n: round(v, 5) for n, v in stage_ms.items()},
+                  "event_ms_per_step": round(layer_ev_ms, 5)},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(pr, logits, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,209 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) mixture-of-experts layer forward.
+ *
+ * One MoE layer on one GPU's share of the work: router logits, softmax top-k
+ * gating, dispatch of token slots into expert-sorted order, each local
+ * expert's SwiGLU feed-forward network as a grouped GEMM over ragged
+ * per-expert segments, and the gate-weighted combine back to token order.
+ * The share is either all E experts, or one expert-parallel rank's block of
+ * E_l consecutive experts [expert_begin, expert_begin + E_l) seeing all T
+ * tokens.
+ *
+ * Where the operations come from:
+ *  - "Wide Expert Parallelism" (llm-d notes, kodekloud), section "What is an
+ *    MoE layer?": a small gate looks at each token and routes it to a small
+ *    subset of many independent experts (DeepSeek-R1: 8 of 256).
+ *  - "Expert Parallelism for MoE Models" (apxml), section "Mechanics of Token
+ *    Routing and All-to-All Communication": the token representation travels
+ *    to where its expert lives, the expert computes, the output travels back.
+ *  - "Serving MoE models with expert parallelism on 8xH200" (reviosa),
+ *    section "Tensor parallel vs expert parallel": a GPU owns whole experts
+ *    (256 on 8 GPUs: 32 each) and runs full-size expert GEMMs on the tokens
+ *    dispatched to it.
+ * The pages fix neither the gate formula nor the expert network.  This
+ * library computes (exactly, up to floating-point rounding):
+ *    L[t,e]   = sum_c x[t,c] W_r[c,e] + b[e]                 (float32 accumulate)
+ *    idx[t,:] = the k experts with the largest L[t,.], ordered by (-L, e):
+ *               ties go to the lower expert index
+ *    w[t,i]   = exp(L[t,idx_i] - m) / sum_j exp(L[t,idx_j] - m), m = L[t,idx_0]
+ *               (softmax over all E, renormalised over the k chosen)
+ *    FFN_e(v) = (silu(v Wg_e) * (v Wu_e)) Wd_e,   silu(z) = z / (1 + exp(-z))
+ *    out[t]   = sum_{i < k, idx[t,i] local} w[t,i] FFN_{idx[t,i]}(x[t])   (in i order)
+ *
+ * Conventions for every call
+ *  - All device arrays are row-major, 16-byte aligned, owned by the caller
+ *    and must stay valid until the stream work completes.  The library never
+ *    allocates, frees or synchronises; it keeps no state between calls and
+ *    is re-entrant.  Scratch memory comes from the caller (moe_workspace_size).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Every call only enqueues kernels on it and returns.
+ *  - A slot is s = t*k + i (token t, its i-th chosen expert).  Expert ids in
+ *    index arrays are global ids in [0, E).
+ *  - Formats: activations and the router matrix are MOE_F32 or MOE_BF16;
+ *    expert weights are MOE_F32, MOE_BF16, or MOE_FP8_E4M3 (OCP E4M3FN codes,
+ *    one byte each) with float32 scales per 128x128 block of the stored
+ *    matrix.  Supported (act, weight) pairs: (F32, F32), (BF16, BF16),
+ *    (BF16, FP8_E4M3).  Accumulation is float32; intermediate h is rounded
+ *    to the activation format.
+ *  - Expert weights are stored "out x in" (the math matrices transposed):
+ *      w_gate, w_up : [E_l][F][d]      w_down : [E_l][d][F]
+ *      s_gate, s_up : [E_l][F/128][d/128]   s_down : [E_l][d/128][F/128]
+ *    so that Wg_e[c][f] = w_gate[e - expert_begin][f][c] (times its scale).
+ *
+ * Errors: every call checks its arguments on the host before enqueuing
+ * anything and returns MOE_ERR_INVALID_ARGUMENT (null required pointer, a
+ * size out of range, d or F not a multiple of 128, expert_begin + num_local
+ * > E), MOE_ERR_UNSUPPORTED (an unsupported format pair or a size above the
+ * stated limits) or MOE_ERR_WORKSPACE_TOO_SMALL.  A failed kernel launch
+ * returns MOE_ERR_HIP.  On a device, an expert id outside [0, E) in a
+ * caller-supplied topk_idx is treated as not local (it never faults).  No
+ * C++ exception crosses this interface.
+ *
+ * Limits: 1 <= k <= E <= 512; T*k < 2^31; d, F multiples of 128 and
+ * at most 65536; T = 0 is accepted and enqueues nothing (no output is written).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+  MOE_ERR_HIP = 4
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype_t;
+
+/* Which call a workspace is sized for. */
+typedef enum { MOE_CALL_PERMUTE = 0, MOE_CALL_EXPERT_FFN = 1, MOE_CALL_FORWARD = 2 } moe_call_t;
+
+/* Problem shape.  T tokens, hidden size d, E global experts, top-k, SwiGLU
+ * width F, local expert block [expert_begin, expert_begin + num_local);
+ * act / weight hold moe_dtype_t values. */
+typedef struct {
+  int32_t T, d, E, k, F;
+  int32_t expert_begin, num_local;
+  int32_t act, weight;
+} moe_problem_t;
+
+/* Bytes of scratch `call` needs for problem p (0 if p is invalid).  The
+ * scratch must be device memory, 256-byte aligned; its contents on entry do
+ * not matter and are undefined on return. */
+size_t moe_workspace_size(const moe_problem_t* p, int32_t call);
+
+/* Static, human-readable name of a status code. */
+const char* moe_status_string(moe_status_t s);
+
+/* Router and gate ("What is an MoE layer?": the gate picks a few experts per
+ * token).
+ *  x        [T][d] act format.
+ *  w_router [d][E] act format, or NULL: then `logits` is an INPUT [T][E]
+ *           float32 and only selection and gates run.
+ *  router_bias [E] float32 or NULL (zero): added to the logits, so it moves
+ *           both the selection and the gate values.
+ *  logits   [T][E] float32 output (L including the bias) or NULL when not
+ *           wanted (only allowed with w_router != NULL).
+ *  topk_idx [T][k] int32 output: global expert ids ordered by (-L, e).
+ *  topk_w   [T][k] float32 output: renormalised gates (sum to 1 per token).
+ * The selection is taken on exactly the float32 values written to `logits`. */
+moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* w_router,
+                       const float* router_bias, float* logits, int32_t* topk_idx,
+                       float* topk_w, void* stream);
+
+/* Dispatch order ("Mechanics of Token Routing": tokens go to their expert):
+ * a stable counting sort of the slots whose expert is local.
+ *  topk_idx    [T*k] int32 input.
+ *  counts      [E_l] int32 output: kept slots per local expert.
+ *  offsets     [E_l + 1] int32 output: exclusive prefix of counts;
+ *              offsets[E_l] = N, the number of kept slots.
+ *  sorted_slot [T*k] int32 output: rows 0..N-1 hold the kept slots grouped
+ *              by local expert, increasing s inside each group; rows N.. are
+ *              left unspecified.
+ *  slot_pos    [T*k] int32 output: position of slot s in sorted_slot, or -1
+ *              if s is not kept.
+ *  ws / ws_bytes: scratch of at least moe_workspace_size(p, MOE_CALL_PERMUTE). */
+moe_status_t moe_permute(const moe_problem_t* p, const int32_t* topk_idx, int32_t* counts,
+                         int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* Local experts ("Tensor parallel vs expert parallel": full-size expert
+ * GEMMs on the dispatched tokens): for every kept row p < offsets[E_l], with
+ * s = sorted_slot[p], t = s / k and j the local expert whose segment
+ * [offsets[j], offsets[j+1]) holds p:
+ *    y[p] = FFN_{expert_begin + j}(x[t]) * (topk_w ? topk_w[s] : 1)
+ *  x           [T][d] act format.
+ *  sorted_slot [T*k], offsets [E_l + 1]: as produced by moe_permute.
+ *  w_gate, w_up [E_l][F][d], w_down [E_l][d][F] in the weight format.
+ *  s_gate, s_up, s_down: block scales (required for FP8_E4M3, else ignored).
+ *  topk_w      [T*k] float32 gates or NULL (y left unweighted).
+ *  y           [T*k][d] act format output; rows >= N are not written.
+ *  ws / ws_bytes: scratch of at least moe_workspace_size(p, MOE_CALL_EXPERT_FFN). */
+moe_status_t moe_expert_ffn(const moe_problem_t* p, const void* x, const int32_t* sorted_slot,
+                            const int32_t* offsets, const void* w_gate, const void* w_up,
+                            const void* w_down, const float* s_gate, const float* s_up,
+                            const float* s_down, const float* topk_w, void* y, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/* Combine ("Mechanics of Token Routing": the output travels back), without
+ * atomics, in a fixed order:
+ *    out[t] = sum_{i = 0..k-1, slot_pos[t*k+i] >= 0} y[slot_pos[t*k+i]] * (topk_w ? topk_w[t*k+i] : 1)
+ * accumulated in float32 in increasing i and rounded once to the act format;
+ * a token with no kept slot gets 0.
+ *  y [T*k][d] act format; slot_pos [T*k]; topk_w [T*k] float32 or NULL
+ *  (y already weighted); out [T][d] act format output. */
+moe_status_t moe_combine(const moe_problem_t* p, const void* y, const int32_t* slot_pos,
+                         const float* topk_w, void* out, void* stream);
+
+/* Arguments of moe_forward.  Required: x, w_gate, w_up, w_down, out, and
+ * either w_router, or logits as an input.  s_* are required for FP8 weights.
+ * The remaining outputs are optional (NULL = not wanted) and hold what the
+ * individual calls above would write. */
+typedef struct {
+  const void* x;            /* [T][d] act */
+  const void* w_router;     /* [d][E] act, or NULL (logits is then an input) */
+  const float* router_bias; /* [E] or NULL */
+  const void* w_gate;       /* [E_l][F][d] weight format */
+  const void* w_up;         /* [E_l][F][d] */
+  const void* w_down;       /* [E_l][d][F] */
+  const float* s_gate;      /* FP8 block scales, see above */
+  const float* s_up;
+  const float* s_down;
+  void* out;                /* [T][d] act output */
+  float* logits;            /* [T][E] output (or input when w_router == NULL) */
+  int32_t* topk_idx;        /* [T][k] */
+  float* topk_w;            /* [T][k] */
+  int32_t* counts;          /* [E_l] */
+  int32_t* offsets;         /* [E_l + 1] */
+  int32_t* sorted_slot;     /* [T*k] */
+  int32_t* slot_pos;        /* [T*k] */
+  /* Optional stage timing: NULL, or MOE_FORWARD_EVENTS hipEvent_t handles
+   * (created by the caller, passed as void*) that moe_forward records on
+   * `stream` at the stage boundaries: [0] before the router, [1] after the
+   * router, [2] after the permutation, [3] after the expert tile schedule,
+   * [4] after the gate/up GEMM, [5] after the down GEMM, [6] after the
+   * combine.  A failed record returns MOE_ERR_HIP. */
+  void* const* events;
+} moe_forward_args_t;
+
+#define MOE_FORWARD_EVENTS 7
+
+/* The whole layer: route, permute, expert FFN (gates folded into the down
+ * projection's epilogue), combine.  No host synchronisation: the
+ * data-dependent sizes (counts, N) never return to the host.
+ *  ws / ws_bytes: scratch of at least moe_workspace_size(p, MOE_CALL_FORWARD). */
+moe_status_t moe_forward(const moe_problem_t* p, const moe_forward_args_t* a, void* ws,
+                         size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

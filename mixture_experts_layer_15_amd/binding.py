@@ -1,0 +1,159 @@
+"""Thin ctypes binding of the C ABI in ``include/moe.h``.
+
+Argument marshalling only: tensors become device pointers, the stream becomes
+the current HIP stream, status codes become exceptions.  Every step of the
+layer runs in the HIP library; there is no fallback of any kind.  PyTorch is
+used for device memory and streams.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe_mi355x.so")
+
+MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16, MOE_FP8_E4M3 = range(3)
+MOE_CALL_PERMUTE, MOE_CALL_EXPERT_FFN, MOE_CALL_FORWARD = range(3)
+MOE_FORWARD_EVENTS = 7
+
+FMT = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
+
+
+class MoEError(RuntimeError):
+    def __init__(self, call: str, status: int, text: str):
+        super().__init__(f"{call} failed: {text} ({status})")
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("T", "d", "E", "k", "F", "expert_begin", "num_local", "act", "weight")]
+
+
+class ForwardArgs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("x", "w_router", "router_bias", "w_gate", "w_up", "w_down", "s_gate", "s_up",
+                 "s_down", "out", "logits", "topk_idx", "topk_w", "counts", "offsets",
+                 "sorted_slot", "slot_pos", "events")]
+
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the built library; raise if it is missing (no fallback exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it first with "
+                          "`python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+    P = ctypes.POINTER(Problem)
+    lib.moe_workspace_size.argtypes = [P, i32]
+    lib.moe_workspace_size.restype = sz
+    lib.moe_status_string.argtypes = [ctypes.c_int]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_route.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+    lib.moe_permute.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_expert_ffn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_combine.argtypes = [P, vp, vp, vp, vp, vp]
+    lib.moe_forward.argtypes = [P, ctypes.POINTER(ForwardArgs), vp, sz, vp]
+    for f in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward"):
+        getattr(lib, f).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def problem(T, d, E, k, F, expert_begin=0, num_local=None, act="bf16", weight="bf16") -> Problem:
+    num_local = E - expert_begin if num_local is None else num_local
+    return Problem(T, d, E, k, F, expert_begin, num_local,
+                   FMT[act] if isinstance(act, str) else act,
+                   FMT[weight] if isinstance(weight, str) else weight)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(call: str, status: int) -> None:
+    if status != MOE_OK:
+        text = load_library().moe_status_string(status).decode()
+        raise MoEError(call, status, text)
+
+
+def moe_status_string(status: int) -> str:
+    return load_library().moe_status_string(status).decode()
+
+
+def moe_workspace_size(p: Problem, call: int) -> int:
+    return int(load_library().moe_workspace_size(ctypes.byref(p), call))
+
+
+def moe_route(p, x, w_router, router_bias, logits, topk_idx, topk_w, stream=None) -> None:
+    st = load_library().moe_route(ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(router_bias),
+                                  _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _stream(stream))
+    _check("moe_route", st)
+
+
+def moe_permute(p, topk_idx, counts, offsets, sorted_slot, slot_pos, ws, stream=None) -> None:
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = load_library().moe_permute(ctypes.byref(p), _ptr(topk_idx), _ptr(counts), _ptr(offsets),
+                                    _ptr(sorted_slot), _ptr(slot_pos), _ptr(ws), nbytes,
+                                    _stream(stream))
+    _check("moe_permute", st)
+
+
+def moe_expert_ffn(p, x, sorted_slot, offsets, w_gate, w_up, w_down, s_gate, s_up, s_down,
+                   topk_w, y, ws, stream=None) -> None:
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = load_library().moe_expert_ffn(
+        ctypes.byref(p), _ptr(x), _ptr(sorted_slot), _ptr(offsets), _ptr(w_gate), _ptr(w_up),
+        _ptr(w_down), _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(topk_w), _ptr(y), _ptr(ws),
+        nbytes, _stream(stream))
+    _check("moe_expert_ffn", st)
+
+
+def moe_combine(p, y, slot_pos, topk_w, out, stream=None) -> None:
+    st = load_library().moe_combine(ctypes.byref(p), _ptr(y), _ptr(slot_pos), _ptr(topk_w),
+                                    _ptr(out), _stream(stream))
+    _check("moe_combine", st)
+
+
+def moe_forward(p, *, x, w_router, router_bias, w_gate, w_up, w_down, out, ws,
+                s_gate=None, s_up=None, s_down=None, logits=None, topk_idx=None, topk_w=None,
+                counts=None, offsets=None, sorted_slot=None, slot_pos=None, events=None,
+                stream=None) -> None:
+    """``events``: None, or a ctypes array of MOE_FORWARD_EVENTS hipEvent_t handles."""
+    a = ForwardArgs(_ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w_gate), _ptr(w_up),
+                    _ptr(w_down), _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(out), _ptr(logits),
+                    _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(sorted_slot),
+                    _ptr(slot_pos), None if events is None else ctypes.addressof(events))
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = load_library().moe_forward(ctypes.byref(p), ctypes.byref(a), _ptr(ws), nbytes,
+                                    _stream(stream))
+    _check("moe_forward", st)
+
+
+def workspace(p: Problem, call: int, device="cuda") -> torch.Tensor:
+    """A device scratch tensor of the size the library asks for (torch memory)."""
+    n = moe_workspace_size(p, call)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)

@@ -1,0 +1,82 @@
+// Combine: gate-weighted sum of each token's expert outputs, back in token
+// order, without atomics.
+//
+// "Expert Parallelism for MoE Models" (apxml), section "Mechanics of Token
+// Routing and All-to-All Communication": after the expert computes, its output
+// is sent back to the token.  out[t] = sum over i of the kept slots t*k + i of
+// y[slot_pos[t*k + i]] (times the gate when y is unweighted), accumulated in
+// float32 in increasing i and rounded once.  A token with no kept slot gets 0.
+//
+// One workgroup per token row; each thread owns 8 consecutive columns (one
+// 16-byte bf16 chunk, or two 16-byte float32 chunks), so every y row is read
+// with full-width coalesced loads.  The pass is HBM-bound.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <bool kBF16>
+__global__ __launch_bounds__(kThreads) void combine_kernel(const void* y, const int32_t* slot_pos,
+                                                           const float* topk_w, void* out, int d,
+                                                           int k) {
+  const long long t = blockIdx.x;
+  for (int c0 = threadIdx.x * 8; c0 < d; c0 += kThreads * 8) {
+    float acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+    for (int i = 0; i < k; ++i) {
+      const long long s = t * k + i;
+      const int p = slot_pos[s];
+      if (p < 0) continue;
+      const float gw = topk_w ? topk_w[s] : 1.0f;
+      if constexpr (kBF16) {
+        const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(y) +
+                                                        (long long)p * d + c0);
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] = fmaf(bf16_to_f32(uint16_t(u[q] & 0xffff)), gw, acc[2 * q]);
+          acc[2 * q + 1] = fmaf(bf16_to_f32(uint16_t(u[q] >> 16)), gw, acc[2 * q + 1]);
+        }
+      } else {
+        const float* yr = static_cast<const float*>(y) + (long long)p * d + c0;
+        const float4 v0 = *reinterpret_cast<const float4*>(yr);
+        const float4 v1 = *reinterpret_cast<const float4*>(yr + 4);
+        const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = fmaf(f[q], gw, acc[q]);
+      }
+    }
+    if constexpr (kBF16) {
+      uint4 o;
+      o.x = pack_bf16x2(acc[0], acc[1]);
+      o.y = pack_bf16x2(acc[2], acc[3]);
+      o.z = pack_bf16x2(acc[4], acc[5]);
+      o.w = pack_bf16x2(acc[6], acc[7]);
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + t * d + c0) = o;
+    } else {
+      float* orow = static_cast<float*>(out) + t * d + c0;
+      *reinterpret_cast<float4*>(orow) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      *reinterpret_cast<float4*>(orow + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t combine(const Shape& s, const void* y, const int32_t* slot_pos, const float* topk_w,
+                   void* out, hipStream_t st) {
+  if (s.T == 0) return hipSuccess;
+  if (s.act == kBF16)
+    hipLaunchKernelGGL(combine_kernel<true>, dim3(s.T), dim3(kThreads), 0, st, y, slot_pos, topk_w,
+                       out, s.d, s.k);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, dim3(s.T), dim3(kThreads), 0, st, y, slot_pos,
+                       topk_w, out, s.d, s.k);
+  return hipGetLastError();
+}
+
+}  // namespace moe

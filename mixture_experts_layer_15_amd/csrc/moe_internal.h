@@ -1,0 +1,48 @@
+// Internal host-side interface between the C ABI (moe_api.cpp) and the
+// kernel launchers (*.hip).  Not installed; callers use include/moe.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+enum Fmt : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
+
+constexpr int kMaxExperts = 512;      // E limit (router top-k and permutation LDS tables)
+constexpr int kPermuteChunk = 2048;   // slots per workgroup in the permutation kernels
+
+// Validated problem shape.  S = T*k slots.
+struct Shape {
+  int T, d, E, k, F, e0, El;
+  int act, weight;
+  long long S;
+};
+
+inline size_t align_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
+inline int act_bytes(const Shape& s) { return s.act == kF32 ? 4 : 2; }
+
+// ---- route.hip
+hipError_t route(const Shape& s, const void* x, const void* w_router, const float* bias,
+                 const float* logits_in, float* logits_out, int32_t* topk_idx, float* topk_w,
+                 hipStream_t st);
+
+// ---- permute.hip
+size_t permute_ws_bytes(const Shape& s);
+hipError_t permute(const Shape& s, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                   int32_t* sorted_slot, int32_t* slot_pos, void* ws, hipStream_t st);
+
+// ---- ffn.hip
+size_t ffn_ws_bytes(const Shape& s);
+hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
+                      const int32_t* offsets, const void* w_gate, const void* w_up,
+                      const void* w_down, const float* s_gate, const float* s_up,
+                      const float* s_down, const float* topk_w, void* y, void* ws,
+                      hipStream_t st, hipEvent_t const* stage_events = nullptr);
+
+// ---- combine.hip
+hipError_t combine(const Shape& s, const void* y, const int32_t* slot_pos, const float* topk_w,
+                   void* out, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,154 @@
+// Dispatch order: a stable counting sort of the kept slots by local expert.
+//
+// "Expert Parallelism for MoE Models" (apxml), section "Mechanics of Token
+// Routing and All-to-All Communication": each token is sent to the device
+// that hosts its expert.  On one device that is a gather into expert-sorted
+// order.  The sort has one correct result: the slots of each local expert in
+// increasing slot index s = t*k + i.
+//
+// Three kernels, none with an order-dependent atomic:
+//   1. hist:    each workgroup counts the kept slots of its 2048-slot chunk per
+//               local expert (LDS counters; counting is order-free).
+//   2. scan:    one workgroup sums the chunk counts per expert, scans them into
+//               `offsets`, and turns the chunk counts into each chunk's first
+//               position inside every expert segment.
+//   3. scatter: each workgroup walks its chunk in slot order, 256 slots per
+//               round; a slot's rank among equal experts inside its wave comes
+//               from ballots over the expert id bits, across waves from
+//               per-wave counts in LDS, across rounds from a running base.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kChunk = kPermuteChunk;   // slots per workgroup
+constexpr int kThreads = 256;
+constexpr int kRounds = kChunk / kThreads;
+
+__global__ __launch_bounds__(kThreads) void permute_hist_kernel(const int32_t* __restrict__ idx,
+                                                                long long S, int e0, int El,
+                                                                int nb, int32_t* blk_cnt) {
+  __shared__ int hist[kMaxExperts];
+  const int b = blockIdx.x;
+  for (int e = threadIdx.x; e < El; e += kThreads) hist[e] = 0;
+  __syncthreads();
+  const long long base = (long long)b * kChunk;
+  for (int r = 0; r < kRounds; ++r) {
+    const long long s = base + r * kThreads + threadIdx.x;
+    if (s < S) {
+      const int e = idx[s] - e0;
+      if ((unsigned)e < (unsigned)El) atomicAdd(&hist[e], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < El; e += kThreads) blk_cnt[(size_t)e * nb + b] = hist[e];
+}
+
+// One workgroup of kMaxExperts threads: thread e owns local expert e.
+__global__ __launch_bounds__(kMaxExperts) void permute_scan_kernel(int El, int nb, int32_t* blk,
+                                                                   int32_t* counts,
+                                                                   int32_t* offsets) {
+  __shared__ int sums[kMaxExperts];
+  const int e = threadIdx.x;
+  int cnt = 0;
+  if (e < El)
+    for (int b = 0; b < nb; ++b) cnt += blk[(size_t)e * nb + b];
+  sums[e] = cnt;
+  __syncthreads();
+  // inclusive Hillis-Steele scan over the experts
+  for (int o = 1; o < kMaxExperts; o <<= 1) {
+    const int v = e >= o ? sums[e - o] : 0;
+    __syncthreads();
+    sums[e] += v;
+    __syncthreads();
+  }
+  const int excl = sums[e] - cnt;
+  if (e < El) {
+    counts[e] = cnt;
+    offsets[e] = excl;
+    int run = excl;
+    for (int b = 0; b < nb; ++b) {
+      const int c = blk[(size_t)e * nb + b];
+      blk[(size_t)e * nb + b] = run;
+      run += c;
+    }
+  }
+  if (e == El - 1) offsets[El] = sums[e];
+}
+
+__global__ __launch_bounds__(kThreads) void permute_scatter_kernel(
+    const int32_t* __restrict__ idx, long long S, int e0, int El, int nbits, int nb,
+    const int32_t* __restrict__ blk_off, int32_t* sorted_slot, int32_t* slot_pos) {
+  __shared__ int base[kMaxExperts];
+  __shared__ int wcnt[kThreads / kWave][kMaxExperts];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int w = tid / kWave;
+  const int l = lane_id();
+  for (int e = tid; e < El; e += kThreads) {
+    base[e] = blk_off[(size_t)e * nb + b];
+#pragma unroll
+    for (int q = 0; q < kThreads / kWave; ++q) wcnt[q][e] = 0;
+  }
+  __syncthreads();
+  const unsigned long long below = (1ull << l) - 1ull;
+  for (int r = 0; r < kRounds; ++r) {
+    const long long s = (long long)b * kChunk + r * kThreads + tid;
+    const bool valid = s < S;
+    int e = valid ? idx[s] - e0 : -1;
+    const bool keep = valid && (unsigned)e < (unsigned)El;
+    if (valid && !keep) slot_pos[s] = -1;
+    // lanes of this wave holding the same local expert
+    unsigned long long m = __ballot(keep);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool on = keep && ((e >> bit) & 1);
+      const unsigned long long v = __ballot(on);
+      m &= on ? v : ~v;
+    }
+    const int rank = __popcll(m & below);
+    const int cnt = __popcll(m);
+    if (keep && rank == 0) wcnt[w][e] = cnt;
+    __syncthreads();
+    if (keep) {
+      int pos = base[e] + rank;
+      for (int q = 0; q < w; ++q) pos += wcnt[q][e];
+      sorted_slot[pos] = (int32_t)s;
+      slot_pos[s] = pos;
+    }
+    __syncthreads();
+    if (keep && rank == 0) {
+      atomicAdd(&base[e], cnt);  // a sum: the result does not depend on order
+      wcnt[w][e] = 0;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+size_t permute_ws_bytes(const Shape& s) {
+  const long long nb = (s.S + kChunk - 1) / kChunk;
+  return align_up((size_t)nb * s.El * sizeof(int32_t));
+}
+
+hipError_t permute(const Shape& s, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                   int32_t* sorted_slot, int32_t* slot_pos, void* ws, hipStream_t st) {
+  const int nb = (int)((s.S + kChunk - 1) / kChunk);
+  int32_t* blk = static_cast<int32_t*>(ws);
+  int nbits = 0;
+  while ((1 << nbits) < s.El) ++nbits;
+  if (nb > 0) {
+    hipLaunchKernelGGL(permute_hist_kernel, dim3(nb), dim3(kThreads), 0, st, topk_idx, s.S, s.e0,
+                       s.El, nb, blk);
+  }
+  hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kMaxExperts), 0, st, s.El, nb, blk, counts,
+                     offsets);
+  if (nb > 0) {
+    hipLaunchKernelGGL(permute_scatter_kernel, dim3(nb), dim3(kThreads), 0, st, topk_idx, s.S,
+                       s.e0, s.El, nbits, nb, blk, sorted_slot, slot_pos);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -121,9 +121,9 @@ def dequant_block128(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     R, C = q.shape
     assert R % BLOCK == 0 and C % BLOCK == 0
     assert s.shape == (R // BLOCK, C // BLOCK)
-    w = e4m3fn_to_f64(q)
-    scale = np.repeat(np.repeat(np.asarray(s, dtype=np.float64), BLOCK, axis=0), BLOCK, axis=1)
-    return w * scale
+    w = e4m3fn_to_f64(q).reshape(R // BLOCK, BLOCK, C // BLOCK, BLOCK)
+    w *= np.asarray(s, dtype=np.float64)[:, None, :, None]   # s[r // 128, c // 128]
+    return w.reshape(R, C)
 
 
 def decode_act(a: np.ndarray, fmt: str) -> np.ndarray:

@@ -1,0 +1,154 @@
+"""The C ABI library: it loads, exports every declared symbol, and rejects
+bad arguments on the host before anything is enqueued.  No call here reaches
+a kernel launch, so the suite runs without a GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from mixture_experts_layer_15_amd import binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from mixture_experts_layer_15_amd import build
+        build.build()
+    return B.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_five_calls_and_helpers():
+    names = declared_functions()
+    for n in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
+              "moe_workspace_size", "moe_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (moe_\w+)", out))
+    for n in declared_functions():
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_no_torch_or_cxx_types_in_the_header():
+    text = open(HEADER).read()
+    assert "torch" not in text and "at::" not in text and "std::" not in text
+    assert 'extern "C"' in text
+
+
+def _p(**kw):
+    base = dict(T=64, d=256, E=8, k=2, F=256, expert_begin=0, num_local=8, act="bf16", weight="bf16")
+    base.update(kw)
+    return B.problem(**base)
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails its host checks
+
+
+@pytest.mark.parametrize("kw", [dict(k=0), dict(k=9), dict(T=-1), dict(d=100), dict(F=200),
+                                dict(expert_begin=4, num_local=5), dict(num_local=0),
+                                dict(expert_begin=-1), dict(act=7), dict(E=0)])
+def test_invalid_shapes_rejected(lib, kw):
+    p = _p(**kw)
+    st = lib.moe_route(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, FAKE, None)
+    assert st == B.MOE_ERR_INVALID_ARGUMENT
+    assert B.moe_workspace_size(p, B.MOE_CALL_FORWARD) == 0
+
+
+@pytest.mark.parametrize("act,weight", [("f32", "bf16"), ("bf16", "f32"), ("f32", "fp8"),
+                                        ("fp8", "fp8"), ("fp8", "bf16")])
+def test_unsupported_format_pairs(lib, act, weight):
+    p = _p(act=act, weight=weight)
+    st = lib.moe_combine(ctypes.byref(p), FAKE, FAKE, None, FAKE, None)
+    assert st == B.MOE_ERR_UNSUPPORTED
+
+
+def test_limits_are_unsupported_not_invalid(lib):
+    p = _p(E=1024, k=2, num_local=1024)
+    assert lib.moe_combine(ctypes.byref(p), FAKE, FAKE, None, FAKE, None) == B.MOE_ERR_UNSUPPORTED
+    p = _p(T=2 ** 30, k=2)
+    assert lib.moe_combine(ctypes.byref(p), FAKE, FAKE, None, FAKE, None) == B.MOE_ERR_UNSUPPORTED
+
+
+def test_null_required_pointers(lib):
+    p = _p()
+    assert lib.moe_route(ctypes.byref(p), FAKE, FAKE, None, None, None, FAKE, None) == 1
+    assert lib.moe_route(ctypes.byref(p), None, None, None, None, FAKE, FAKE, None) == 1
+    assert lib.moe_permute(ctypes.byref(p), None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == 1
+    assert lib.moe_combine(ctypes.byref(p), FAKE, None, None, FAKE, None) == 1
+    assert lib.moe_expert_ffn(ctypes.byref(p), FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None,
+                              None, None, FAKE, FAKE, 1 << 30, None) == 1
+    p8 = _p(weight="fp8")
+    assert lib.moe_expert_ffn(ctypes.byref(p8), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+                              None, None, FAKE, FAKE, 1 << 30, None) == 1
+    assert lib.moe_forward(ctypes.byref(p), None, FAKE, 1 << 30, None) == 1
+    args = B.ForwardArgs()
+    args.x = args.w_gate = args.w_up = args.w_down = args.out = FAKE   # no router, no logits
+    assert lib.moe_forward(ctypes.byref(p), ctypes.byref(args), FAKE, 1 << 30, None) == 1
+
+
+def test_workspace_too_small(lib):
+    p = _p()
+    for call, fn in ((B.MOE_CALL_PERMUTE, "perm"), (B.MOE_CALL_EXPERT_FFN, "ffn"),
+                     (B.MOE_CALL_FORWARD, "fwd")):
+        need = B.moe_workspace_size(p, call)
+        assert need > 0 and need % 256 == 0
+        if fn == "perm":
+            st = lib.moe_permute(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None)
+        elif fn == "ffn":
+            st = lib.moe_expert_ffn(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+                                    None, None, FAKE, FAKE, need - 1, None)
+        else:
+            a = B.ForwardArgs()
+            a.x = a.w_router = a.w_gate = a.w_up = a.w_down = a.out = FAKE
+            st = lib.moe_forward(ctypes.byref(p), ctypes.byref(a), FAKE, need - 1, None)
+        assert st == B.MOE_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_zero_tokens_enqueue_nothing(lib):
+    p = _p(T=0)
+    ws_need = B.moe_workspace_size(p, B.MOE_CALL_FORWARD)
+    assert lib.moe_route(ctypes.byref(p), FAKE, FAKE, None, None, FAKE, FAKE, None) == 0
+    assert lib.moe_combine(ctypes.byref(p), FAKE, FAKE, None, FAKE, None) == 0
+    a = B.ForwardArgs()
+    a.x = a.w_router = a.w_gate = a.w_up = a.w_down = a.out = FAKE
+    assert lib.moe_forward(ctypes.byref(p), ctypes.byref(a), FAKE, ws_need, None) == 0
+
+
+def test_workspace_grows_with_the_problem(lib):
+    small = B.moe_workspace_size(_p(T=64), B.MOE_CALL_FORWARD)
+    big = B.moe_workspace_size(_p(T=4096), B.MOE_CALL_FORWARD)
+    assert big > small
+    # the forward scratch holds y [T*k][d] at least
+    assert big >= 4096 * 2 * 256 * 2
+
+
+def test_status_strings(lib):
+    for code, name in [(0, "MOE_OK"), (1, "MOE_ERR_INVALID_ARGUMENT"), (2, "MOE_ERR_UNSUPPORTED"),
+                       (3, "MOE_ERR_WORKSPACE_TOO_SMALL"), (4, "MOE_ERR_HIP")]:
+        assert B.moe_status_string(code) == name
+
+
+def test_product_code_never_imports_the_oracle():
+    pat = re.compile(r"^\s*(from\s+oracle\b|import\s+oracle\b)|moe_oracle|oracle/", re.M)
+    pkg = os.path.dirname(B.__file__)
+    for root, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                assert not pat.search(open(os.path.join(root, f)).read()), f
+    # in bench.py only the cpu_baseline leg may use it
+    bench = open(os.path.join(os.path.dirname(pkg), "bench.py")).read()
+    assert len(re.findall(r"from oracle import", bench)) <= 1
