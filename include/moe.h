@@ -109,8 +109,9 @@ const char* moe_status_string(moe_status_t s);
  *           float32 and only selection and gates run.
  *  router_bias [E] float32 or NULL (zero): added to the logits, so it moves
  *           both the selection and the gate values.
- *  logits   [T][E] float32 output (L including the bias) or NULL when not
- *           wanted (only allowed with w_router != NULL).
+ *  logits   [T][E] float32, required: the output L (including the bias)
+ *           when w_router != NULL (it also serves as the router's scratch),
+ *           the input when w_router == NULL.
  *  topk_idx [T][k] int32 output: global expert ids ordered by (-L, e).
  *  topk_w   [T][k] float32 output: renormalised gates (sum to 1 per token).
  * The selection is taken on exactly the float32 values written to `logits`. */

@@ -397,6 +397,15 @@ size_t max_tiles(const Shape& s, int bm) { return (size_t)((s.S + bm - 1) / bm) 
 
 }  // namespace
 
+FfnSchedule ffn_schedule_view(const Shape& s, void* ws) {
+  unsigned char* p = static_cast<unsigned char*>(ws);
+  FfnSchedule v;
+  v.tiles = reinterpret_cast<int2*>(p);
+  v.ntiles = reinterpret_cast<int*>(p + align_up(max_tiles(s, 32) * sizeof(int2)));
+  v.bm = tile_bm(s);
+  return v;
+}
+
 size_t ffn_ws_bytes(const Shape& s) {
   // schedule (at the smallest tile) + tile count + h [S][F]
   return align_up(max_tiles(s, 32) * sizeof(int2)) + align_up(sizeof(int)) +
@@ -407,19 +416,21 @@ hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
                       const int32_t* offsets, const void* w_gate, const void* w_up,
                       const void* w_down, const float* s_gate, const float* s_up,
                       const float* s_down, const float* topk_w, void* y, void* ws,
-                      hipStream_t st, hipEvent_t const* ev) {
+                      hipStream_t st, bool schedule_ready, hipEvent_t const* ev) {
   if (s.S == 0) return hipSuccess;
-  unsigned char* p = static_cast<unsigned char*>(ws);
-  int2* tiles = reinterpret_cast<int2*>(p);
-  p += align_up(max_tiles(s, 32) * sizeof(int2));
-  int* ntiles = reinterpret_cast<int*>(p);
-  p += align_up(sizeof(int));
-  uint16_t* h = reinterpret_cast<uint16_t*>(p);
-
-  const int bm = tile_bm(s);
-  hipLaunchKernelGGL(ffn_schedule_kernel, dim3(1), dim3(kMaxExperts), 0, st, offsets, s.El, bm,
-                     tiles, ntiles);
-  hipError_t e = hipGetLastError();
+  const FfnSchedule sv = ffn_schedule_view(s, ws);
+  int2* tiles = sv.tiles;
+  int* ntiles = sv.ntiles;
+  uint16_t* h = reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(ws) +
+                                            align_up(max_tiles(s, 32) * sizeof(int2)) +
+                                            align_up(sizeof(int)));
+  const int bm = sv.bm;
+  hipError_t e = hipSuccess;
+  if (!schedule_ready) {
+    hipLaunchKernelGGL(ffn_schedule_kernel, dim3(1), dim3(kMaxExperts), 0, st, offsets, s.El, bm,
+                       tiles, ntiles);
+    e = hipGetLastError();
+  }
   if (e == hipSuccess && ev) e = hipEventRecord(ev[0], st);
   if (e != hipSuccess) return e;
 

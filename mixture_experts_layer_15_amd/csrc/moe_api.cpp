@@ -48,7 +48,7 @@ moe_status_t from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 
 // Device-memory layout of the moe_forward workspace.
 struct ForwardLayout {
-  size_t logits, idx, w, counts, offsets, sorted, pos, y, permute, ffn, total;
+  size_t logits, idx, w, counts, offsets, sorted, pos, y, router, permute, ffn, total;
 };
 
 ForwardLayout forward_layout(const Shape& s) {
@@ -67,6 +67,7 @@ ForwardLayout forward_layout(const Shape& s) {
   L.sorted = take((size_t)s.S * sizeof(int32_t));
   L.pos = take((size_t)s.S * sizeof(int32_t));
   L.y = take((size_t)s.S * s.d * moe::act_bytes(s));
+  L.router = take(moe::route_ws_bytes(s));
   L.permute = take(moe::permute_ws_bytes(s));
   L.ffn = take(moe::ffn_ws_bytes(s));
   L.total = o;
@@ -116,12 +117,12 @@ moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* w_rout
   if (st != MOE_OK) return st;
   if (topk_idx == nullptr || topk_w == nullptr) return MOE_ERR_INVALID_ARGUMENT;
   if (w_router != nullptr && x == nullptr) return MOE_ERR_INVALID_ARGUMENT;
-  if (w_router == nullptr && logits == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+  if (logits == nullptr) return MOE_ERR_INVALID_ARGUMENT;
   if (s.T == 0) return MOE_OK;
+  // without scratch, the router's partial products go straight to `logits`
   const float* lin = w_router == nullptr ? logits : nullptr;
-  float* lout = w_router == nullptr ? nullptr : logits;
-  return from_hip(moe::route(s, x, w_router, router_bias, lin, lout, topk_idx, topk_w,
-                             static_cast<hipStream_t>(stream)));
+  return from_hip(moe::route(s, x, w_router, router_bias, lin, logits, topk_idx, topk_w, logits,
+                             1, static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_permute(const moe_problem_t* p, const int32_t* topk_idx, int32_t* counts,
@@ -206,14 +207,18 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_forward_args_t* a, vo
   auto mark = [&](int i) { return a->events ? hipEventRecord(ev[i], strm) : hipSuccess; };
   hipError_t e = mark(0);
   if (e == hipSuccess)
-    e = moe::route(s, a->x, a->w_router, a->router_bias, lin, lout, idx, gw, strm);
+    e = moe::route(s, a->x, a->w_router, a->router_bias, lin, lout, idx, gw,
+                   reinterpret_cast<float*>(base + L.router), moe::router_splits(s), strm);
   if (e == hipSuccess) e = mark(1);
+  const moe::FfnSchedule sched = moe::ffn_schedule_view(s, base + L.ffn);
+  bool sched_ready = false;
   if (e == hipSuccess)
-    e = moe::permute(s, idx, counts, offsets, sorted, pos, base + L.permute, strm);
+    e = moe::permute(s, idx, counts, offsets, sorted, pos, base + L.permute, strm, &sched,
+                     &sched_ready);
   if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess)
     e = moe::expert_ffn(s, a->x, sorted, offsets, a->w_gate, a->w_up, a->w_down, a->s_gate,
-                        a->s_up, a->s_down, gw, y, base + L.ffn, strm,
+                        a->s_up, a->s_down, gw, y, base + L.ffn, strm, sched_ready,
                         a->events ? ev + 3 : nullptr);
   if (e == hipSuccess) e = moe::combine(s, y, pos, nullptr, a->out, strm);
   if (e == hipSuccess) e = mark(6);

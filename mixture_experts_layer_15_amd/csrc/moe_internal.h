@@ -24,22 +24,42 @@ inline size_t align_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
 inline int act_bytes(const Shape& s) { return s.act == kF32 ? 4 : 2; }
 
 // ---- route.hip
+// K splits of the router GEMM used by moe_forward, and the scratch they need.
+int router_splits(const Shape& s);
+size_t route_ws_bytes(const Shape& s);
+// w_router != null: partial products go to `partials` ([nsplit][T][E]; may be
+// `logits` itself when nsplit == 1), then logits = sum + bias are published to
+// `logits` (if non-null) and selected on.  w_router == null: `logits_in` holds
+// the final logits.
 hipError_t route(const Shape& s, const void* x, const void* w_router, const float* bias,
-                 const float* logits_in, float* logits_out, int32_t* topk_idx, float* topk_w,
-                 hipStream_t st);
+                 const float* logits_in, float* logits, int32_t* topk_idx, float* topk_w,
+                 float* partials, int nsplit, hipStream_t st);
 
-// ---- permute.hip
-size_t permute_ws_bytes(const Shape& s);
-hipError_t permute(const Shape& s, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
-                   int32_t* sorted_slot, int32_t* slot_pos, void* ws, hipStream_t st);
-
-// ---- ffn.hip
+// ---- ffn.hip (tile schedule shared with the permutation)
+struct FfnSchedule {
+  int2* tiles;   // (local expert, first row) of every M tile
+  int* ntiles;   // number of M tiles
+  int bm;        // M tile height
+};
+FfnSchedule ffn_schedule_view(const Shape& s, void* ffn_ws);
 size_t ffn_ws_bytes(const Shape& s);
+// schedule_ready: the tile schedule in ffn_ws was already written (by the
+// permutation); stage_events: null or 3 events recorded after the schedule,
+// the gate/up GEMM and the down GEMM.
 hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
                       const int32_t* offsets, const void* w_gate, const void* w_up,
                       const void* w_down, const float* s_gate, const float* s_up,
                       const float* s_down, const float* topk_w, void* y, void* ws,
-                      hipStream_t st, hipEvent_t const* stage_events = nullptr);
+                      hipStream_t st, bool schedule_ready = false,
+                      hipEvent_t const* stage_events = nullptr);
+
+// ---- permute.hip
+size_t permute_ws_bytes(const Shape& s);
+// When `sched` is non-null and the single-workgroup path runs, the expert
+// tile schedule is written too and *sched_written is set.
+hipError_t permute(const Shape& s, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                   int32_t* sorted_slot, int32_t* slot_pos, void* ws, hipStream_t st,
+                   const FfnSchedule* sched = nullptr, bool* sched_written = nullptr);
 
 // ---- combine.hip
 hipError_t combine(const Shape& s, const void* y, const int32_t* slot_pos, const float* topk_w,

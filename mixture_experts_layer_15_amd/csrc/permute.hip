@@ -16,6 +16,9 @@
 //               round; a slot's rank among equal experts inside its wave comes
 //               from ballots over the expert id bits, across waves from
 //               per-wave counts in LDS, across rounds from a running base.
+// A decode batch has few slots (T*k <= 8192): then one workgroup of 16 waves
+// runs all three phases in one kernel, and also writes the expert GEMM's tile
+// schedule (the M tiles of every expert segment), saving four launches.
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -125,6 +128,90 @@ __global__ __launch_bounds__(kThreads) void permute_scatter_kernel(
   }
 }
 
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallWaves = kSmallThreads / kWave;
+constexpr long long kSmallSlots = 8192;
+
+__global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(
+    const int32_t* __restrict__ idx, int S, int e0, int El, int nbits, int32_t* counts,
+    int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos, int bm, int2* tiles, int* ntiles) {
+  __shared__ int hist[kMaxExperts];
+  __shared__ int base[kMaxExperts];
+  __shared__ int scan[kSmallThreads];
+  __shared__ int wcnt[kSmallWaves][kMaxExperts];
+  const int tid = threadIdx.x;
+  const int w = tid / kWave;
+  const int l = lane_id();
+  for (int e = tid; e < El; e += kSmallThreads) {
+    hist[e] = 0;
+#pragma unroll
+    for (int q = 0; q < kSmallWaves; ++q) wcnt[q][e] = 0;
+  }
+  __syncthreads();
+  for (int s = tid; s < S; s += kSmallThreads) {
+    const int e = idx[s] - e0;
+    if ((unsigned)e < (unsigned)El) atomicAdd(&hist[e], 1);
+  }
+  __syncthreads();
+  // exclusive scan of the counts (and of the M tiles per expert)
+  const int cnt = tid < El ? hist[tid] : 0;
+  const int nt = (cnt + bm - 1) / bm;
+  scan[tid] = cnt | (nt << 16);  // both fit: cnt <= 8192, nt <= 8192
+  __syncthreads();
+  for (int o = 1; o < kSmallThreads; o <<= 1) {
+    const int v = tid >= o ? scan[tid - o] : 0;
+    __syncthreads();
+    scan[tid] += v;
+    __syncthreads();
+  }
+  const int incl = scan[tid];
+  const int off = (incl & 0xffff) - cnt;
+  const int tfirst = (incl >> 16) - nt;
+  if (tid < El) {
+    counts[tid] = cnt;
+    offsets[tid] = off;
+    base[tid] = off;
+    if (tiles)
+      for (int i = 0; i < nt; ++i) tiles[tfirst + i] = make_int2(tid, off + i * bm);
+  }
+  if (tid == El - 1) {
+    offsets[El] = incl & 0xffff;
+    if (tiles) *ntiles = incl >> 16;
+  }
+  __syncthreads();
+  // stable scatter, 1024 slots per round in slot order
+  const unsigned long long below = (1ull << l) - 1ull;
+  for (int r0 = 0; r0 < S; r0 += kSmallThreads) {
+    const int s = r0 + tid;
+    const bool valid = s < S;
+    const int e = valid ? idx[s] - e0 : -1;
+    const bool keep = valid && (unsigned)e < (unsigned)El;
+    if (valid && !keep) slot_pos[s] = -1;
+    unsigned long long m = __ballot(keep);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool on = keep && ((e >> bit) & 1);
+      const unsigned long long v = __ballot(on);
+      m &= on ? v : ~v;
+    }
+    const int rank = __popcll(m & below);
+    const int c = __popcll(m);
+    if (keep && rank == 0) wcnt[w][e] = c;
+    __syncthreads();
+    if (keep) {
+      int pos = base[e] + rank;
+      for (int q = 0; q < w; ++q) pos += wcnt[q][e];
+      sorted_slot[pos] = s;
+      slot_pos[s] = pos;
+    }
+    __syncthreads();
+    if (keep && rank == 0) {
+      atomicAdd(&base[e], c);  // a sum: the result does not depend on order
+      wcnt[w][e] = 0;
+    }
+    __syncthreads();
+  }
+}
+
 }  // namespace
 
 size_t permute_ws_bytes(const Shape& s) {
@@ -133,11 +220,22 @@ size_t permute_ws_bytes(const Shape& s) {
 }
 
 hipError_t permute(const Shape& s, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
-                   int32_t* sorted_slot, int32_t* slot_pos, void* ws, hipStream_t st) {
-  const int nb = (int)((s.S + kChunk - 1) / kChunk);
-  int32_t* blk = static_cast<int32_t*>(ws);
+                   int32_t* sorted_slot, int32_t* slot_pos, void* ws, hipStream_t st,
+                   const FfnSchedule* sched, bool* sched_written) {
+  if (sched_written) *sched_written = false;
   int nbits = 0;
   while ((1 << nbits) < s.El) ++nbits;
+  if (s.S <= kSmallSlots) {
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kSmallThreads), 0, st, topk_idx,
+                       (int)s.S, s.e0, s.El, nbits, counts, offsets, sorted_slot, slot_pos,
+                       sched ? sched->bm : 1, sched ? sched->tiles : nullptr,
+                       sched ? sched->ntiles : nullptr);
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && sched_written) *sched_written = sched != nullptr;
+    return e;
+  }
+  const int nb = (int)((s.S + kChunk - 1) / kChunk);
+  int32_t* blk = static_cast<int32_t*>(ws);
   if (nb > 0) {
     hipLaunchKernelGGL(permute_hist_kernel, dim3(nb), dim3(kThreads), 0, st, topk_idx, s.S, s.e0,
                        s.El, nb, blk);

@@ -7,252 +7,281 @@
 // softmax over the k chosen logits (a softmax over all E renormalised over
 // the chosen k: the full denominator cancels).
 //
-// One workgroup owns 32 tokens and every expert column.  bf16: the router
-// GEMM runs on MFMA 32x32x16 with the K dimension split four ways across the
-// waves (each wave streams a quarter of W_r, staged through LDS in its natural
-// [k][e] layout), and the four partial tiles are added in a fixed order.  The
-// float32 logits of the tile stay in LDS, so selection and gates happen in the
-// same kernel on exactly the values written to `logits`.
+// Two kernels:
+//  * router_partial: workgroup (row tile of 32 tokens, K split) computes the
+//    32 x E partial product over its K range on MFMA 32x32x16 (bf16) or with
+//    float32 FMAs (f32).  Inside a workgroup the four waves take interleaved
+//    32-deep K steps, each wave staging its own W_r rows through a private LDS
+//    buffer in W_r's natural [k][e] layout, with the next step's global loads
+//    in flight while the current step computes.  The four wave partials are
+//    added in a fixed order.  Splitting K across workgroups gives a decode
+//    batch (T = 64) enough workgroups to cover the chip.
+//  * router_topk: one wave per token adds the K-split partials in a fixed
+//    order plus the bias, publishes the float32 logits, and selects the top k
+//    on exactly those values; gates are exp(L_i - L_0) normalised over the k.
+// Every sum has a fixed order, so the logits (and hence the routing) are
+// bit-reproducible from run to run.
 #include "moe_device.h"
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int kBM = 32;        // tokens per workgroup
+constexpr int kBM = 32;        // tokens per partial workgroup
 constexpr int kCC = 128;       // expert columns per pass (4 MFMA blocks of 32)
-constexpr int kBK = 32;        // K rows of W_r per wave per step
+constexpr int kBK = 32;        // K rows of W_r per wave step
 constexpr int kThreads = 256;  // 4 waves
-constexpr int kStageStride = kCC + 8;  // bf16 elements per staged W_r row (padded)
+constexpr int kStageStride = kCC + 8;  // bf16 per staged W_r row (padded)
+constexpr int kStageElems = kBK * kStageStride;
 
-struct RouteArgs {
+struct PartialArgs {
   const void* x;         // [T][d]
-  const void* w_router;  // [d][E] or null
-  const float* bias;     // [E] or null
-  const float* logits_in;  // [T][E] (when w_router is null)
-  float* logits_out;     // [T][E] or null
-  int32_t* topk_idx;     // [T][k]
-  float* topk_w;         // [T][k]
-  int T, d, E, k;
+  const void* w_router;  // [d][E]
+  float* out;            // [nsplit][T][E] partial sums
+  int T, d, E;
+  int k_per_split;       // multiple of 128
 };
 
-// LDS: a 64 KB region that holds the W_r staging tiles during the K loop and
-// the four partial tiles afterwards, then the [32][E] float32 logit tile.
-constexpr int kRegionBytes = 4 * kBM * kCC * 4;  // 64 KB
+// Global loads of one 32-deep K step: W_r rows k0 + (l / 16) + 4 i, columns
+// c0 + 8 (l % 16) .. +8, and this lane's two A fragments.
+#define MOE_ROUTER_LOAD(STEP)                                                                 \
+  do {                                                                                        \
+    const int k0_ = kbeg + (STEP) * kBK;                                                      \
+    if (full) {                                                                               \
+      _Pragma("unroll") for (int i = 0; i < 8; ++i) rw[i] =                                   \
+          *reinterpret_cast<const u32x4_t*>(wr + (size_t)(k0_ + sr + 4 * i) * a.E + c0 + sc); \
+    } else {                                                                                  \
+      _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                         \
+        uint32_t h_[4];                                                                       \
+        _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                       \
+          const int col_ = c0 + sc + 2 * j;                                                   \
+          const uint16_t* src_ = wr + (size_t)(k0_ + sr + 4 * i) * a.E + col_;                \
+          const uint32_t lo_ = col_ < a.E ? src_[0] : 0u;                                     \
+          const uint32_t hi_ = col_ + 1 < a.E ? src_[1] : 0u;                                 \
+          h_[j] = lo_ | (hi_ << 16);                                                          \
+        }                                                                                     \
+        rw[i] = u32x4_t{h_[0], h_[1], h_[2], h_[3]};                                          \
+      }                                                                                       \
+    }                                                                                         \
+    ra0 = *reinterpret_cast<const bf16x8_t*>(xrow + k0_ + kgrp);                              \
+    ra1 = *reinterpret_cast<const bf16x8_t*>(xrow + k0_ + 16 + kgrp);                         \
+  } while (0)
 
-// bf16 router GEMM for one 128-column pass; leaves the finished logits of
-// columns [c0, c0 + 128) in lg[r][c].
-__device__ void router_pass_bf16(const RouteArgs& a, int t0, int c0, unsigned char* region,
-                                 float* lg, int lgs) {
+// LDS: the four wave stages during the K loop, then the four wave partials.
+constexpr int kRouterLds = 4 * kBM * kCC * 4;  // 64 KB
+static_assert(4 * kStageElems * 2 <= kRouterLds, "stages fit the shared region");
+
+__global__ __launch_bounds__(kThreads) void router_partial_bf16(PartialArgs a) {
+  __shared__ __align__(16) unsigned char smem[kRouterLds];
+  uint16_t (*stage)[kStageElems] = reinterpret_cast<uint16_t (*)[kStageElems]>(smem);
+  float (*red)[kBM][kCC] = reinterpret_cast<float (*)[kBM][kCC]>(smem);
   const int tid = threadIdx.x;
   const int w = tid / kWave;
   const int l = lane_id();
+  const int t0 = blockIdx.x * kBM;
+  const int split = blockIdx.y;
+  const int kbeg = split * a.k_per_split;
+  const int nsteps = a.k_per_split / kBK;  // multiple of 4
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
   const uint16_t* wr = static_cast<const uint16_t*>(a.w_router);
-  uint16_t* stage = reinterpret_cast<uint16_t*>(region) + w * kBK * kStageStride;
+  uint16_t* st = stage[w];
+  float* out = a.out + (size_t)split * a.T * a.E;
 
-  f32x16_t acc[4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) acc[b] = f32x16_t{};
-
-  // A operand rows: lane l serves token row l % 32 (clamped to T-1).
+  // A rows: lane l serves token row l % 32 (clamped), 8 K values at 8 (l / 32).
   const int arow = min(t0 + (l & 31), a.T - 1);
   const uint16_t* xrow = x + (size_t)arow * a.d;
-  const int kgrp = (l >> 5) * 8;  // which 8 of the 16 K values this lane holds
+  const int kgrp = (l >> 5) * 8;
+  const int sr = l >> 4, sc = (l & 15) * 8;
 
-  const int nks = a.d / kBK;
-  for (int ks0 = 0; ks0 < nks; ks0 += 4) {
-    const int ks = ks0 + w;
-    const bool active = ks < nks;
-    __syncthreads();  // previous step's readers are done with the staging tile
-    if (active) {
-      // Stage W_r[k0 .. k0+32)[c0 .. c0+128) : 32 rows x 256 bytes; lane l copies
-      // 16 bytes of row (l / 16) + 4 i, columns 8 (l % 16) .. +8.
-      const int k0 = ks * kBK;
+  for (int c0 = 0; c0 < a.E; c0 += kCC) {
+    const bool full = (a.E & 7) == 0 && c0 + kCC <= a.E;  // wave-uniform
+    f32x16_t acc[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = (l >> 4) + 4 * i;
-        const int c = (l & 15) * 8;
-        const uint16_t* src = wr + (size_t)(k0 + r) * a.E + c0 + c;
-        uint16_t* dst = stage + r * kStageStride + c;
-        if ((a.E & 7) == 0 && c0 + c + 8 <= a.E) {
-          *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
-        } else {
+    for (int b = 0; b < 4; ++b) acc[b] = f32x16_t{};
+    u32x4_t rw[8];
+    bf16x8_t ra0, ra1;
+
+    int step = w;
+    if (step < nsteps) MOE_ROUTER_LOAD(step);
+    for (; step < nsteps; step += 4) {
+      // registers -> this wave's private LDS stage.  LDS executes one wave's
+      // operations in order, so the previous step's reads of the stage are
+      // done before these writes land, and these writes before the reads
+      // below; the empty asm only keeps the compiler from moving LDS accesses
+      // across.
 #pragma unroll
-          for (int j = 0; j < 8; ++j) dst[j] = (c0 + c + j < a.E) ? src[j] : uint16_t(0);
-        }
-      }
-    }
-    __syncthreads();
-    if (active) {
-      const int k0 = ks * kBK;
+      for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<u32x4_t*>(st + (sr + 4 * i) * kStageStride + sc) = rw[i];
+      const bf16x8_t a0 = ra0, a1 = ra1;
+      asm volatile("" ::: "memory");
+      if (step + 4 < nsteps) MOE_ROUTER_LOAD(step + 4);
 #pragma unroll
-      for (int kk = 0; kk < kBK; kk += 16) {
-        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(xrow + k0 + kk + kgrp);
+      for (int h = 0; h < 2; ++h) {
+        const bf16x8_t av = h ? a1 : a0;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const int col = b * 32 + (l & 31);
           uint16_t e[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) e[j] = stage[(kk + kgrp + j) * kStageStride + col];
-          uint4 pk = make_uint4(e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16),
-                                e[4] | (uint32_t(e[5]) << 16), e[6] | (uint32_t(e[7]) << 16));
-          const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, pk);
-          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[b], 0, 0, 0);
+          for (int j = 0; j < 8; ++j) e[j] = st[(h * 16 + kgrp + j) * kStageStride + col];
+          const u32x4_t pk = {e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16),
+                              e[4] | (uint32_t(e[5]) << 16), e[6] | (uint32_t(e[7]) << 16)};
+          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8_t, pk),
+                                                           acc[b], 0, 0, 0);
         }
       }
+      asm volatile("" ::: "memory");
     }
-  }
-  __syncthreads();
-  // Partial tiles -> LDS red[w][32][128] (MFMA 32x32 output layout: lane l holds
-  // column l % 32, rows 8 (i / 4) + 4 (l / 32) + i % 4).
-  float* red = reinterpret_cast<float*>(region);
+    // wave partials -> LDS (MFMA 32x32 layout: lane l holds column l % 32,
+    // rows 8 (i / 4) + 4 (l / 32) + i % 4), then a fixed-order sum
+    __syncthreads();  // every wave is done with its stage (same LDS)
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = 8 * (i >> 2) + 4 * (l >> 5) + (i & 3);
-      red[(w * kBM + r) * kCC + b * 32 + (l & 31)] = acc[b][i];
+      for (int i = 0; i < 16; ++i)
+        red[w][8 * (i >> 2) + 4 * (l >> 5) + (i & 3)][b * 32 + (l & 31)] = acc[b][i];
+    __syncthreads();
+    for (int o = tid; o < kBM * kCC; o += kThreads) {
+      const int r = o / kCC, c = o % kCC;
+      if (t0 + r < a.T && c0 + c < a.E)
+        out[(size_t)(t0 + r) * a.E + c0 + c] =
+            ((red[0][r][c] + red[1][r][c]) + red[2][r][c]) + red[3][r][c];
     }
+    __syncthreads();
   }
-  __syncthreads();
-  for (int o = tid; o < kBM * kCC; o += kThreads) {
-    const int r = o / kCC, c = o % kCC;
-    if (c0 + c >= a.E) continue;
-    float v = red[(0 * kBM + r) * kCC + c];
-    v += red[(1 * kBM + r) * kCC + c];
-    v += red[(2 * kBM + r) * kCC + c];
-    v += red[(3 * kBM + r) * kCC + c];
-    lg[r * lgs + c0 + c] = v;
-  }
-  __syncthreads();
 }
+#undef MOE_ROUTER_LOAD
 
-// float32 router: each thread forms whole dot products in order over c.
-__device__ void router_f32(const RouteArgs& a, int t0, float* lg, int lgs) {
+// float32 router: each thread forms whole dot products over its K range in order.
+__global__ __launch_bounds__(kThreads) void router_partial_f32(PartialArgs a) {
   const float* x = static_cast<const float*>(a.x);
   const float* wr = static_cast<const float*>(a.w_router);
+  const int t0 = blockIdx.x * kBM;
+  const int kbeg = blockIdx.y * a.k_per_split;
+  float* out = a.out + (size_t)blockIdx.y * a.T * a.E;
   for (int o = threadIdx.x; o < kBM * a.E; o += kThreads) {
     const int r = o / a.E, e = o % a.E;
-    const int t = min(t0 + r, a.T - 1);
+    const int t = t0 + r;
+    if (t >= a.T) continue;
     const float* xr = x + (size_t)t * a.d;
     float acc = 0.f;
-    for (int c = 0; c < a.d; ++c) acc = fmaf(xr[c], wr[(size_t)c * a.E + e], acc);
-    lg[r * lgs + e] = acc;
+    for (int c = kbeg; c < kbeg + a.k_per_split; ++c)
+      acc = fmaf(xr[c], wr[(size_t)c * a.E + e], acc);
+    out[(size_t)t * a.E + e] = acc;
   }
-  __syncthreads();
 }
 
-template <bool kBF16>
-__global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char* region = smem;
-  float* lg = reinterpret_cast<float*>(smem + kRegionBytes);
-  const int lgs = a.E;  // row stride of the logit tile
-  const int t0 = blockIdx.x * kBM;
-  const int tid = threadIdx.x;
-
-  if (a.w_router == nullptr) {
-    for (int o = tid; o < kBM * a.E; o += kThreads) {
-      const int r = o / a.E, e = o % a.E;
-      const int t = min(t0 + r, a.T - 1);
-      lg[r * lgs + e] = a.logits_in[(size_t)t * a.E + e];
-    }
-    __syncthreads();
-  } else {
-    if constexpr (kBF16) {
-      for (int c0 = 0; c0 < a.E; c0 += kCC) router_pass_bf16(a, t0, c0, region, lg, lgs);
-    } else {
-      router_f32(a, t0, lg, lgs);
-    }
-    // bias, then publish the exact float32 values the selection will use
-    for (int o = tid; o < kBM * a.E; o += kThreads) {
-      const int r = o / a.E, e = o % a.E;
-      float v = lg[r * lgs + e];
-      if (a.bias) v += a.bias[e];
-      lg[r * lgs + e] = v;
-      if (a.logits_out && t0 + r < a.T) a.logits_out[(size_t)(t0 + r) * a.E + e] = v;
-    }
-    __syncthreads();
-  }
-
-  // Top-k and gates: wave w handles rows 8w .. 8w+7.
-  const int w = tid / kWave;
+// One wave per token: logits = sum of the split partials (in split order) +
+// bias; then top-k by (-L, e) and the renormalised gates.
+__global__ __launch_bounds__(kThreads) void router_topk_kernel(const float* part, int nsplit,
+                                                               const float* bias,
+                                                               float* logits_out, int T, int E,
+                                                               int k, int32_t* topk_idx,
+                                                               float* topk_w) {
+  const int w = threadIdx.x / kWave;
   const int l = lane_id();
-  const int per_lane = (a.E + kWave - 1) / kWave;  // <= 8 for E <= 512
-  for (int rr = 0; rr < kBM / 4; ++rr) {
-    const int r = w * (kBM / 4) + rr;
-    const int t = t0 + r;
-    if (t >= a.T) break;
-    const float* row = lg + r * lgs;
-    uint32_t taken = 0;  // bit j: expert l + 64 j already chosen
-    float first = 0.f;
-    float mine[8];       // chosen logit i is held by lane i % 64 in slot i / 64
+  const int t = blockIdx.x * (kThreads / kWave) + w;
+  if (t >= T) return;
+  constexpr int kPerLane = kMaxExperts / kWave;  // 8
+  float v[kPerLane];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) mine[q] = 0.f;
-    for (int i = 0; i < a.k; ++i) {
-      float bv = -INFINITY;
-      int be = 0x7fffffff;
-      for (int j = 0; j < per_lane; ++j) {
-        const int e = l + kWave * j;
-        if (e >= a.E || ((taken >> j) & 1u)) continue;
-        float v = row[e];
-        if (v != v) v = -INFINITY;  // NaN never wins (inputs are expected finite)
-        if (v > bv || (v == bv && e < be)) { bv = v; be = e; }
-      }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, kWave);
-        const int oe = __shfl_xor(be, o, kWave);
-        if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-      }
-      if ((be & (kWave - 1)) == l) taken |= 1u << (be / kWave);
-      if (i == 0) first = bv;
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-        if (i == q * kWave + l) mine[q] = bv;
-      if (l == 0) a.topk_idx[(size_t)t * a.k + i] = be;
+  for (int j = 0; j < kPerLane; ++j) {
+    const int e = l + kWave * j;
+    float s = -INFINITY;
+    if (e < E) {
+      s = part[(size_t)t * E + e];
+      for (int q = 1; q < nsplit; ++q) s += part[((size_t)q * T + t) * E + e];
+      if (bias) s += bias[e];
+      if (logits_out) logits_out[(size_t)t * E + e] = s;
+      if (s != s) s = -INFINITY;  // NaN never wins (inputs are expected finite)
     }
-    // gates: exp(L_i - L_0) / sum over the chosen, summed in a fixed tree order
-    float part = 0.f;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      if (q * kWave + l < a.k) {
-        mine[q] = expf(mine[q] - first);
-        part += mine[q];
-      }
-    }
-    const float tot = wave_sum(part);
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-      if (q * kWave + l < a.k) a.topk_w[(size_t)t * a.k + q * kWave + l] = mine[q] / tot;
+    v[j] = s;
   }
+  uint32_t taken = 0;  // bit j: expert l + 64 j already chosen
+  float first = 0.f;
+  float mine[kPerLane];  // chosen logit i is held by lane i % 64 in slot i / 64
+#pragma unroll
+  for (int q = 0; q < kPerLane; ++q) mine[q] = 0.f;
+  for (int i = 0; i < k; ++i) {
+    float bv = -INFINITY;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) {
+      const int e = l + kWave * j;
+      if (e < E && !((taken >> j) & 1u) && (v[j] > bv || (v[j] == bv && e < be))) {
+        bv = v[j];
+        be = e;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, kWave);
+      const int oe = __shfl_xor(be, o, kWave);
+      if (ov > bv || (ov == bv && oe < be)) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if ((be & (kWave - 1)) == l) taken |= 1u << (be / kWave);
+    if (i == 0) first = bv;
+#pragma unroll
+    for (int q = 0; q < kPerLane; ++q)
+      if (i == q * kWave + l) mine[q] = bv;
+    if (l == 0) topk_idx[(size_t)t * k + i] = be;
+  }
+  float psum = 0.f;
+#pragma unroll
+  for (int q = 0; q < kPerLane; ++q) {
+    if (q * kWave + l < k) {
+      mine[q] = expf(mine[q] - first);
+      psum += mine[q];
+    }
+  }
+  const float tot = wave_sum(psum);
+#pragma unroll
+  for (int q = 0; q < kPerLane; ++q)
+    if (q * kWave + l < k) topk_w[(size_t)t * k + q * kWave + l] = mine[q] / tot;
 }
 
 }  // namespace
 
+int router_splits(const Shape& s) {
+  // K splits for about one workgroup per compute unit, each split >= 128 deep
+  const int tiles = (s.T + kBM - 1) / kBM;
+  int splits = 1;
+  while (s.d % (splits * 2 * 128) == 0 && tiles * splits * 2 <= 256) splits *= 2;
+  return splits;
+}
+
+size_t route_ws_bytes(const Shape& s) {
+  return align_up((size_t)router_splits(s) * s.T * s.E * sizeof(float));
+}
+
 hipError_t route(const Shape& s, const void* x, const void* w_router, const float* bias,
-                 const float* logits_in, float* logits_out, int32_t* topk_idx, float* topk_w,
-                 hipStream_t st) {
+                 const float* logits_in, float* logits, int32_t* topk_idx, float* topk_w,
+                 float* partials, int nsplit, hipStream_t st) {
   if (s.T == 0) return hipSuccess;
-  RouteArgs a{x, w_router, bias, logits_in, logits_out, topk_idx, topk_w, s.T, s.d, s.E, s.k};
-  const size_t lds = kRegionBytes + (size_t)kBM * s.E * sizeof(float);
-  const dim3 grid((s.T + kBM - 1) / kBM);
-  static bool attr_set[2] = {false, false};
-  const int which = s.act == kBF16 ? 1 : 0;
-  const void* kern = which ? reinterpret_cast<const void*>(route_kernel<true>)
-                           : reinterpret_cast<const void*>(route_kernel<false>);
-  if (!attr_set[which]) {
-    const int max_lds = kRegionBytes + kBM * kMaxExperts * (int)sizeof(float);
-    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
-    if (e != hipSuccess) return e;
-    attr_set[which] = true;
-  }
-  if (which) {
-    hipLaunchKernelGGL(route_kernel<true>, grid, dim3(kThreads), lds, st, a);
+  const float* part;
+  const float* b = bias;
+  if (w_router == nullptr) {
+    part = logits_in;  // final logits given: no bias, nothing to publish
+    nsplit = 1;
+    b = nullptr;
+    logits = nullptr;
   } else {
-    hipLaunchKernelGGL(route_kernel<false>, grid, dim3(kThreads), lds, st, a);
+    PartialArgs pa{x, w_router, partials, s.T, s.d, s.E, s.d / nsplit};
+    const dim3 grid((s.T + kBM - 1) / kBM, nsplit);
+    if (s.act == kBF16)
+      hipLaunchKernelGGL(router_partial_bf16, grid, dim3(kThreads), 0, st, pa);
+    else
+      hipLaunchKernelGGL(router_partial_f32, grid, dim3(kThreads), 0, st, pa);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    part = partials;
   }
+  const int wpb = kThreads / kWave;
+  hipLaunchKernelGGL(router_topk_kernel, dim3((s.T + wpb - 1) / wpb), dim3(kThreads), 0, st, part,
+                     nsplit, b, logits, s.T, s.E, s.k, topk_idx, topk_w);
   return hipGetLastError();
 }
 

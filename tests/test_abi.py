@@ -87,6 +87,7 @@ def test_null_required_pointers(lib):
     p = _p()
     assert lib.moe_route(ctypes.byref(p), FAKE, FAKE, None, None, None, FAKE, None) == 1
     assert lib.moe_route(ctypes.byref(p), None, None, None, None, FAKE, FAKE, None) == 1
+    assert lib.moe_route(ctypes.byref(p), FAKE, FAKE, None, None, FAKE, FAKE, None) == 1
     assert lib.moe_permute(ctypes.byref(p), None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == 1
     assert lib.moe_combine(ctypes.byref(p), FAKE, None, None, FAKE, None) == 1
     assert lib.moe_expert_ffn(ctypes.byref(p), FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None,
@@ -121,7 +122,7 @@ def test_workspace_too_small(lib):
 def test_zero_tokens_enqueue_nothing(lib):
     p = _p(T=0)
     ws_need = B.moe_workspace_size(p, B.MOE_CALL_FORWARD)
-    assert lib.moe_route(ctypes.byref(p), FAKE, FAKE, None, None, FAKE, FAKE, None) == 0
+    assert lib.moe_route(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == 0
     assert lib.moe_combine(ctypes.byref(p), FAKE, FAKE, None, FAKE, None) == 0
     a = B.ForwardArgs()
     a.x = a.w_router = a.w_gate = a.w_up = a.w_down = a.out = FAKE

@@ -132,6 +132,14 @@ SMALL = {
     "fp8_rank_prefill": synth.WORKLOADS["dsv3_rank"].replace(
         name="fp8_T2000_d512_E16_local0-7_k4_F384", T=2000, d=512, E=16, num_local=8,
         expert_begin=0, k=4, F=384, seed=25),
+    # more than 8192 slots: the multi-workgroup permutation, ragged last chunk
+    "bf16_many_slots": synth.WORKLOADS["prefill"].replace(
+        name="bf16_T3001_d256_E64_k4_F256_zipf", T=3001, d=256, E=64, num_local=64, k=4, F=256,
+        seed=27),
+    # the same on an expert-parallel block (many slots dropped)
+    "fp8_many_slots_rank": synth.WORKLOADS["dsv3_rank"].replace(
+        name="fp8_T2500_d256_E64_local48-63_k6_F256", T=2500, d=256, E=64, num_local=16,
+        expert_begin=48, k=6, F=256, seed=28),
     # f32 with more tiles than the tiny workload
     "f32_tiles": synth.WORKLOADS["tiny"].replace(
         name="f32_T300_d256_E8_k3_F384", T=300, d=256, E=8, num_local=8, k=3, F=384, seed=26),
@@ -241,8 +249,9 @@ def test_standalone_calls_match_forward():
     assert rel_l2(out.float().cpu().numpy(), ref["out"].float().numpy()) <= 1e-2
 
 
-def test_permute_treats_out_of_range_ids_as_not_local():
-    T, E, k, El = 300, 16, 3, 16
+@pytest.mark.parametrize("T", [300, 3001])   # one-workgroup path, and the 3-kernel path
+def test_permute_treats_out_of_range_ids_as_not_local(T):
+    E, k, El = 16, 3, 16
     wl = synth.WORKLOADS["decode"].replace(T=T, d=128, E=E, num_local=El, k=k, F=128)
     p = _prob(wl)
     rng = np.random.default_rng(61)
