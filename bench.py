@@ -98,6 +98,26 @@ class HipEvents:
         return float(out.value)
 
 
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per dispatch of the dominant kernel from the committed
+    rocprofv3 FETCH_SIZE/WRITE_SIZE runs (scaled by the copy-kernel
+    calibration), or None when they were taken on other kernel sources or
+    another workload."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gate_up_decode_pmc.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    m = hashlib.sha256()
+    for f in rec["source_files"]:
+        m.update(open(os.path.join(ROOT, f), "rb").read())
+    if m.hexdigest() != rec["source_sha256"] or rec["workload"] != workload:
+        return None
+    if not rec["kernel"].startswith(kernel):
+        return None
+    return int(rec["traffic_bytes_per_dispatch"])
+
+
 def cpu_baseline(pr: synth.Problem, logits: torch.Tensor, budget_s: float) -> dict:
     """The float64 oracle, as it stands, on whole steps of the same workload
     (or on a token sample when one step would exceed the budget)."""
@@ -231,6 +251,7 @@ def main() -> None:
     nb, wn = (2, 4) if bm == 32 else (4, 2)
     roof["kernel"] = KERNEL_NAMES["gate_up"].format(
         mb=mb, wm=wm, nb=nb, wn=wn, fp8=str(wl.weight == "fp8").lower(), mnb=2 if bm == 32 else 1)
+    roof["traffic"] = measured_traffic(wl.name, roof["kernel"])
     roof["kernel_ms"] = round(stage_ms["gate_up"], 5)
     roof["bytes_per_launch"] = alg["gu_bytes"]
     roof["flop_per_launch"] = alg["gu_flop"]

@@ -56,8 +56,15 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"linking failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB_PATH)
+    # measurement helper: HBM stream / copy probe (bench calibration only)
+    probe = os.path.join(PKG, "moe_bwprobe")
+    cmd = [hipcc(), *COMMON, os.path.join(CSRC, "bwprobe.hip"), "-o", probe + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"building the bandwidth probe failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(probe + ".tmp", probe)
     if verbose:
-        print(f"built {LIB_PATH}", file=sys.stderr)
+        print(f"built {LIB_PATH} and {probe}", file=sys.stderr)
     return LIB_PATH
 
 

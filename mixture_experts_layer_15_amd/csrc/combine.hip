@@ -23,31 +23,49 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void* y, const 
                                                            const float* topk_w, void* out, int d,
                                                            int k) {
   const long long t = blockIdx.x;
+  constexpr int kBatch = 8;  // slots whose rows are loaded together
   for (int c0 = threadIdx.x * 8; c0 < d; c0 += kThreads * 8) {
     float acc[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[q] = 0.f;
-    for (int i = 0; i < k; ++i) {
-      const long long s = t * k + i;
-      const int p = slot_pos[s];
-      if (p < 0) continue;
-      const float gw = topk_w ? topk_w[s] : 1.0f;
-      if constexpr (kBF16) {
-        const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(y) +
-                                                        (long long)p * d + c0);
-        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+    for (int i0 = 0; i0 < k; i0 += kBatch) {
+      int pos[kBatch];
+      float gw[kBatch];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[2 * q] = fmaf(bf16_to_f32(uint16_t(u[q] & 0xffff)), gw, acc[2 * q]);
-          acc[2 * q + 1] = fmaf(bf16_to_f32(uint16_t(u[q] >> 16)), gw, acc[2 * q + 1]);
+      for (int b = 0; b < kBatch; ++b) {
+        const long long s = t * k + i0 + b;
+        pos[b] = i0 + b < k ? slot_pos[s] : -1;
+        gw[b] = (i0 + b < k && topk_w) ? topk_w[s] : 1.0f;
+      }
+      // issue every row load of the batch, then accumulate in increasing i
+      u32x4_t raw[kBatch][kBF16 ? 1 : 2];
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        if (pos[b] < 0) continue;
+        if constexpr (kBF16) {
+          raw[b][0] = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(y) +
+                                                        (long long)pos[b] * d + c0);
+        } else {
+          const float* yr = static_cast<const float*>(y) + (long long)pos[b] * d + c0;
+          raw[b][0] = *reinterpret_cast<const u32x4_t*>(yr);
+          raw[b][1] = *reinterpret_cast<const u32x4_t*>(yr + 4);
         }
-      } else {
-        const float* yr = static_cast<const float*>(y) + (long long)p * d + c0;
-        const float4 v0 = *reinterpret_cast<const float4*>(yr);
-        const float4 v1 = *reinterpret_cast<const float4*>(yr + 4);
-        const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      }
 #pragma unroll
-        for (int q = 0; q < 8; ++q) acc[q] = fmaf(f[q], gw, acc[q]);
+      for (int b = 0; b < kBatch; ++b) {
+        if (pos[b] < 0) continue;
+        if constexpr (kBF16) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t u = raw[b][0][q];
+            acc[2 * q] = fmaf(bf16_to_f32(uint16_t(u & 0xffff)), gw[b], acc[2 * q]);
+            acc[2 * q + 1] = fmaf(bf16_to_f32(uint16_t(u >> 16)), gw[b], acc[2 * q + 1]);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            acc[q] = fmaf(__uint_as_float(raw[b][q >> 2][q & 3]), gw[b], acc[q]);
+        }
       }
     }
     if constexpr (kBF16) {

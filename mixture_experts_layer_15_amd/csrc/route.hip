@@ -183,14 +183,34 @@ __global__ __launch_bounds__(kThreads) void router_topk_kernel(const float* part
   const int t = blockIdx.x * (kThreads / kWave) + w;
   if (t >= T) return;
   constexpr int kPerLane = kMaxExperts / kWave;  // 8
+  constexpr int kBatch = 8;                        // split partials loaded together
   float v[kPerLane];
+#pragma unroll
+  for (int j = 0; j < kPerLane; ++j) v[j] = 0.f;
+  // sum over the splits in split order; each batch's loads are issued together
+  for (int q0 = 0; q0 < nsplit; q0 += kBatch) {
+    float pv[kPerLane][kBatch];
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) {
+      const int e = l + kWave * j;
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b)
+        pv[j][b] = (e < E && q0 + b < nsplit) ? part[((size_t)(q0 + b) * T + t) * E + e] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) {
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        if (q0 + b < nsplit) v[j] = (q0 + b == 0) ? pv[j][b] : v[j] + pv[j][b];
+      }
+    }
+  }
 #pragma unroll
   for (int j = 0; j < kPerLane; ++j) {
     const int e = l + kWave * j;
     float s = -INFINITY;
     if (e < E) {
-      s = part[(size_t)t * E + e];
-      for (int q = 1; q < nsplit; ++q) s += part[((size_t)q * T + t) * E + e];
+      s = v[j];
       if (bias) s += bias[e];
       if (logits_out) logits_out[(size_t)t * E + e] = s;
       if (s != s) s = -INFINITY;  // NaN never wins (inputs are expected finite)
