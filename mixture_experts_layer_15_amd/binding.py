@@ -14,7 +14,7 @@ from typing import Optional
 import torch
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libmoe_mi355x.so")
+LIB_PATH = os.environ.get("MOE_MI355X_LIB", os.path.join(PKG, "libmoe_mi355x.so"))
 
 MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = range(3)

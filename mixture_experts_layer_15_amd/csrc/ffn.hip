@@ -33,7 +33,6 @@
 namespace moe {
 namespace {
 
-constexpr int kBK = 64;  // K elements per pipeline step
 constexpr int kNumXcd = 8;
 
 __global__ __launch_bounds__(kMaxExperts) void ffn_schedule_kernel(const int32_t* offsets, int El,
@@ -73,41 +72,107 @@ struct GemmArgs {
   int K;                       // reduction length
   int Nout;                    // output columns
   int n_tiles_n;               // N tiles per M tile
+  int group_m;                 // M tiles per rasterization group (>= 1)
 };
 
-// Byte offset of 16-byte chunk c (0..7) of row r in a [rows][64] bf16 LDS tile.
-__device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
+// ---- LDS layout of the pipeline stages
+// A stage holds BM rows of kBK bf16 activations and BNW weight rows of kBK K
+// values (bf16, or one byte per FP8 code).  Rows are cut into 16-byte chunks;
+// chunk c of row r sits at physical chunk c ^ swz(r).  The LDS serves a
+// 16-byte read for 16 lanes per cycle over 64 banks (256 B), and an MFMA
+// operand read has those 16 lanes on 16 consecutive rows at one logical
+// chunk.  With R = 256 / row bytes rows per bank sweep and C chunks per row
+// (R * C = 16), swz(r) = (r / R) % C gives the 16 lanes 16 distinct bank
+// groups: r % R picks the sweep slot, r / R the chunk.
+template <int kRowBytes>
+__device__ __forceinline__ int lds_off(int r, int c) {
+  constexpr int C = kRowBytes / 16;
+  constexpr int R = 256 / kRowBytes;
+  static_assert(R * C == 16, "row size");
+  return r * kRowBytes + ((c ^ ((r / R) % C)) << 4);
+}
 
-template <int MB, int WM, int NB, int WN, bool kGateUp, bool kFP8>
+// s_waitcnt that waits until at most N vector-memory operations of this wave
+// (loads, stores, LDS-DMA loads) are outstanding; LGKM and EXP are left alone
+// (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without a memory fence.  LDS-DMA data of a stage is in
+// LDS once the issuing wave's vmcnt wait returns, and LDS executes each
+// wave's operations in order; the empty asm statements keep the compiler from
+// moving memory accesses across the barrier.  (__syncthreads would add a
+// fence that waits for every load in flight, i.e. for all later stages too.)
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One 16-byte global -> LDS load per lane (gfx950 global_load_lds_dwordx4):
+// lane i's 16 bytes land at lds + 16 i; `lds` must be wave-uniform.  The body
+// exists only in the device pass (the host pass never runs it, and clang
+// drops the host launch stubs of kernels that name this builtin directly).
+__device__ __forceinline__ void lds_dma16(const void* src, unsigned char* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+#else
+  (void)src;
+  (void)lds;
+#endif
+}
+
+template <int MB, int WM, int NB, int WN, bool kGateUp, bool kFP8, int kBK, int kStages>
 struct Cfg {
-  static constexpr int kThreads = kWave * WM * WN;
+  static constexpr int kWaves = WM * WN;
+  static constexpr int kThreads = kWave * kWaves;
   static constexpr int BM = 32 * MB * WM;    // tile rows
   static constexpr int BNW = 32 * NB * WN;   // weight rows per tile
-  static constexpr int kAChunks = BM * 8 / kThreads;             // 16-byte A chunks / thread
-  static constexpr int kBChunks = BNW * (kFP8 ? 4 : 8) / kThreads;  // 16-byte B chunks / thread
-  static constexpr int kLdsA = BM * 128;     // bytes per A stage
-  static constexpr int kLdsB = BNW * 128;    // bytes per B stage (bf16 after widening)
-  static constexpr int kLds = 2 * (kLdsA + kLdsB);
-  static_assert(BM * 8 % kThreads == 0 && BNW * (kFP8 ? 4 : 8) % kThreads == 0, "load split");
+  static constexpr int kRowA = kBK * 2;      // bytes per A row per stage
+  static constexpr int kRowB = kBK * (kFP8 ? 1 : 2);
+  static constexpr int kChunksA = kRowA / 16;
+  static constexpr int kChunksB = kRowB / 16;
+  static constexpr int kStageA = BM * kRowA;
+  static constexpr int kStageB = BNW * kRowB;
+  static constexpr int kStage = kStageA + kStageB;
+  static constexpr int kLoadsA = kStageA / (1024 * kWaves);  // 1 KB LDS-DMA loads per wave
+  static constexpr int kLoadsB = kStageB / (1024 * kWaves);
+  static constexpr int kLoads = kLoadsA + kLoadsB;
+  static constexpr int kSteps = kBK / 16;                     // MFMA K steps per stage
+  static constexpr int kScaleSets = kFP8 ? (kGateUp ? 2 : BNW / 128) : 0;
+  static constexpr int kMaxKBlocks = 65536 / 128;
+  static constexpr int kLds = kStages * kStage + kScaleSets * kMaxKBlocks * 4;
+  static_assert(kBK == 32 || kBK == 64, "K step");
+  static_assert(kStageA % (1024 * kWaves) == 0 && kStageB % (1024 * kWaves) == 0, "load split");
   static_assert(!kGateUp || NB % 2 == 0, "gate/up pairs column blocks");
+  static_assert(kStages >= 2 && (kStages - 2) * kLoads < 64, "vmcnt budget");
+  static_assert(kLds <= 160 * 1024, "LDS budget");
+  static_assert(128 % kBK == 0, "a scale block spans whole K steps");
+  static_assert(!kFP8 || !kGateUp || BNW / 2 == 128, "gate/up scales: one 128-row block");
+  static_assert(!kFP8 || BNW % 128 == 0, "down scales: whole 128-row blocks");
 };
 
-template <int MB, int WM, int NB, int WN, bool kGateUp, bool kFP8, int kMinBlocks>
+template <int MB, int WM, int NB, int WN, bool kGateUp, bool kFP8, int kBK, int kStages,
+          int kMinBlocks>
 __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel(GemmArgs a) {
-  using C = Cfg<MB, WM, NB, WN, kGateUp, kFP8>;
-  constexpr int NT = C::kThreads;
+  using C = Cfg<MB, WM, NB, WN, kGateUp, kFP8, kBK, kStages>;
   constexpr int BNW = C::BNW;
+  constexpr int H = NB / 2;  // gate/up: column blocks per half
   extern __shared__ __align__(16) unsigned char smem[];
-  // stage buffers: A0 A1 B0 B1
-  auto ldsA = [&](int buf) { return smem + buf * C::kLdsA; };
-  auto ldsB = [&](int buf) { return smem + 2 * C::kLdsA + buf * C::kLdsB; };
+  float* sc_lds = reinterpret_cast<float*>(smem + kStages * C::kStage);
 
   const int tid = threadIdx.x;
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int l = lane_id();
+  const int g = l >> 5;  // which 8 of an MFMA step's 16 K values this lane holds
   const int wm = wave % WM;
   const int wn = wave / WM;
   const int welem = kFP8 ? 1 : 2;  // bytes per weight element
+  const int nK = a.K / kBK;
+  const int KB = a.K / 128;
 
   // persistent, XCD-contiguous item ranges
   const int n_items = *a.ntiles * a.n_tiles_n;
@@ -117,76 +182,82 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
   const int it_begin = (int)((long long)n_items * xcd / kNumXcd);
   const int it_end = (int)((long long)n_items * (xcd + 1) / kNumXcd);
 
+  // weight-tile row of this lane's MFMA column in block n
+  auto brow = [&](int n) -> int {
+    if (kGateUp) return (n < H ? 0 : BNW / 2) + wn * H * 32 + (n % H) * 32 + (l & 31);
+    return wn * NB * 32 + n * 32 + (l & 31);
+  };
+  const int arow_base = wm * MB * 32 + (l & 31);
+
+  const int n_mtiles = *a.ntiles;
   for (int item = it_begin + slot; item < it_end; item += per_xcd) {
-    const int g = item / a.n_tiles_n;
-    const int nt = item % a.n_tiles_n;
-    const int2 tile = a.tiles[g];
+    // grouped order: items run through groups of group_m consecutive M tiles,
+    // M fastest inside a group, so the workgroups of an XCD that run at the
+    // same time share a few A tiles and a few weight tiles in L2 (instead of
+    // one A tile and as many weight tiles as workgroups)
+    const int per_group = a.group_m * a.n_tiles_n;
+    const int grp = item / per_group;
+    const int first_m = grp * a.group_m;
+    const int gsize = min(a.group_m, n_mtiles - first_m);
+    const int in_grp = item - grp * per_group;
+    const int gt = first_m + in_grp % gsize;
+    const int nt = in_grp / gsize;
+    const int2 tile = a.tiles[gt];
     const int j = tile.x;
     const int row0 = tile.y;
     const int row_end = a.offsets[j + 1];
-    // first output column (gate/up: h column; down: y column) of this tile
-    const int n0 = nt * (kGateUp ? BNW / 2 : BNW);
+    const int n0 = nt * (kGateUp ? BNW / 2 : BNW);  // first output column of the tile
 
-    // ---- per-thread global source pointers for this tile
-    const uint16_t* a_src[C::kAChunks];
+    // ---- this lane's source chunk of every LDS-DMA load of a stage (step 0)
+    const unsigned char* srcA[C::kLoadsA];
 #pragma unroll
-    for (int i = 0; i < C::kAChunks; ++i) {
-      const int q = tid + i * NT;
-      const int r = q >> 3;
+    for (int i = 0; i < C::kLoadsA; ++i) {
+      const int P = (wave * C::kLoadsA + i) * kWave + l;  // 16-byte chunk position
+      const int r = P / C::kChunksA;
+      const int c = (P % C::kChunksA) ^ ((r / (256 / C::kRowA)) % C::kChunksA);
       const int p = min(row0 + r, row_end - 1);
       const long long arow = kGateUp ? (long long)(a.sorted_slot[p] / a.k) : (long long)p;
-      a_src[i] = a.A + arow * a.K + (q & 7) * 8;
+      srcA[i] = reinterpret_cast<const unsigned char*>(a.A + arow * a.K) + c * 16;
     }
-    const unsigned char* b_src[C::kBChunks];
+    const unsigned char* srcB[C::kLoadsB];
 #pragma unroll
-    for (int i = 0; i < C::kBChunks; ++i) {
-      const int q = tid + i * NT;
-      const int r = kFP8 ? (q >> 2) : (q >> 3);  // weight row in tile
-      const int c = kFP8 ? (q & 3) : (q & 7);    // 16-byte chunk in the 64-deep step
+    for (int i = 0; i < C::kLoadsB; ++i) {
+      const int P = (wave * C::kLoadsB + i) * kWave + l;
+      const int r = P / C::kChunksB;
+      const int c = (P % C::kChunksB) ^ ((r / (256 / C::kRowB)) % C::kChunksB);
       const unsigned char* base;
       int wrow;
       if (kGateUp) {
         const bool up = r >= BNW / 2;
-        wrow = n0 + (up ? r - BNW / 2 : r);
+        wrow = min(n0 + (up ? r - BNW / 2 : r), a.Nout - 1);
         base = static_cast<const unsigned char*>(up ? a.W1 : a.W0);
       } else {
         wrow = min(n0 + r, a.Nout - 1);
         base = static_cast<const unsigned char*>(a.W0);
       }
-      b_src[i] = base + ((long long)j * a.Nout + wrow) * a.K * welem + c * 16;
+      srcB[i] = base + ((long long)j * a.Nout + wrow) * a.K * welem + c * 16;
     }
 
-    u32x4_t ra[C::kAChunks];
-    u32x4_t rb[C::kBChunks];
-// global -> registers for K step KS
-#define MOE_GLOAD(KS)                                                                       \
-  do {                                                                                      \
-    _Pragma("unroll") for (int i = 0; i < C::kAChunks; ++i) ra[i] =                         \
-        *reinterpret_cast<const u32x4_t*>(a_src[i] + (KS) * kBK);                           \
-    _Pragma("unroll") for (int i = 0; i < C::kBChunks; ++i) rb[i] =                         \
-        *reinterpret_cast<const u32x4_t*>(b_src[i] + (long long)(KS) * kBK * welem);          \
-  } while (0)
-// registers -> LDS stage BUF (FP8 codes widened to bf16 on the way)
-#define MOE_LSTORE(BUF)                                                                     \
-  do {                                                                                      \
-    _Pragma("unroll") for (int i = 0; i < C::kAChunks; ++i) {                               \
-      const int q = tid + i * NT;                                                           \
-      *reinterpret_cast<u32x4_t*>(ldsA(BUF) + swz(q >> 3, q & 7)) = ra[i];                  \
-    }                                                                                       \
-    _Pragma("unroll") for (int i = 0; i < C::kBChunks; ++i) {                               \
-      const int q = tid + i * NT;                                                           \
-      if constexpr (kFP8) {                                                                 \
-        const int r = q >> 2, c = q & 3;                                                    \
-        const u32x2_t w0 = e4m3x4_to_bf16x4(rb[i].x), w1 = e4m3x4_to_bf16x4(rb[i].y);       \
-        const u32x2_t w2 = e4m3x4_to_bf16x4(rb[i].z), w3 = e4m3x4_to_bf16x4(rb[i].w);       \
-        *reinterpret_cast<u32x4_t*>(ldsB(BUF) + swz(r, 2 * c)) =                            \
-            u32x4_t{w0.x, w0.y, w1.x, w1.y};                                                \
-        *reinterpret_cast<u32x4_t*>(ldsB(BUF) + swz(r, 2 * c + 1)) =                        \
-            u32x4_t{w2.x, w2.y, w3.x, w3.y};                                                \
-      } else {                                                                              \
-        *reinterpret_cast<u32x4_t*>(ldsB(BUF) + swz(q >> 3, q & 7)) = rb[i];                \
-      }                                                                                     \
-    }                                                                                       \
+    stage_barrier();  // every wave is done with the previous item's stages and scales
+    if constexpr (kFP8) {
+      // this tile's block scales -> LDS: set sb holds gate/up (gate/up GEMM) or
+      // the sb-th 128-row block of the tile (down GEMM), for every K block
+      for (int o = tid; o < C::kScaleSets * KB; o += C::kThreads) {
+        const int sb = o / KB, kb = o % KB;
+        const float* S = (kGateUp && sb == 1) ? a.S1 : a.S0;
+        const int nblk = min(kGateUp ? n0 / 128 : n0 / 128 + sb, a.Nout / 128 - 1);
+        sc_lds[sb * C::kMaxKBlocks + kb] = S[((long long)j * (a.Nout / 128) + nblk) * KB + kb];
+      }
+    }
+
+#define MOE_ISSUE_STAGE(KS)                                                                     \
+  do {                                                                                          \
+    unsigned char* sb_ = smem + ((KS) % kStages) * C::kStage;                                   \
+    _Pragma("unroll") for (int i = 0; i < C::kLoadsA; ++i)                                      \
+        lds_dma16(srcA[i] + (long long)(KS) * kBK * 2, sb_ + (wave * C::kLoadsA + i) * 1024);   \
+    _Pragma("unroll") for (int i = 0; i < C::kLoadsB; ++i)                                      \
+        lds_dma16(srcB[i] + (long long)(KS) * kBK * welem,                                      \
+                  sb_ + C::kStageA + (wave * C::kLoadsB + i) * 1024);                            \
   } while (0)
 
     f32x16_t acc[MB][NB];
@@ -202,61 +273,82 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
         for (int n = 0; n < NB; ++n) part[m][n] = f32x16_t{};
     }
 
-    // LDS row of MFMA block rows for this wave
-    const int arow_base = wm * MB * 32 + (l & 31);
-    auto brow = [&](int n) -> int {
-      if (kGateUp) {
-        constexpr int H = NB / 2;
-        return (n < H ? 0 : BNW / 2) + wn * H * 32 + (n % H) * 32 + (l & 31);
-      }
-      return wn * NB * 32 + n * 32 + (l & 31);
-    };
-
-    const int nK = a.K / kBK;
-    __syncthreads();  // LDS of the previous item is no longer read
-    MOE_GLOAD(0);
-    MOE_LSTORE(0);
-    __syncthreads();
-    for (int ks = 0; ks < nK; ++ks) {
-      const int cur = ks & 1;
-      if (ks + 1 < nK) MOE_GLOAD(ks + 1);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int c = kk * 2 + (l >> 5);
-        bf16x8_t af[MB];
+    for (int st = 0; st < kStages - 1; ++st)
+      if (st < nK) MOE_ISSUE_STAGE(st);
+
+    for (int ks = 0; ks < nK; ++ks) {
+      // stage ks has landed once only the later stages' loads remain in flight
+      if (ks + kStages - 2 < nK)
+        wait_vmcnt<(kStages - 2) * C::kLoads>();
+      else
+        wait_vmcnt<0>();
+      stage_barrier();  // all waves' loads of stage ks landed; stage ks-1 is free
+      if (ks + kStages - 1 < nK) MOE_ISSUE_STAGE(ks + kStages - 1);
+
+      const unsigned char* As = smem + (ks % kStages) * C::kStage;
+      const unsigned char* Bs = As + C::kStageA;
+      // K permutation shared by A and B: bf16 weights use chunk 2s + g at step
+      // s; FP8 weights give each lane one 16-byte chunk (16 K values) for two
+      // steps.  Fragments of step s + 1 are read before step s's MFMAs issue.
+      bf16x8_t af[2][MB];
+      bf16x8_t bf[2][kFP8 ? 1 : NB];
+      u32x4_t raw8[kFP8 ? NB : 1];
+      auto read_frags = [&](int s, int buf) {
+        const int cA = kFP8 ? (4 * (s >> 1) + 2 * g + (s & 1)) : (2 * s + g);
 #pragma unroll
         for (int m = 0; m < MB; ++m)
-          af[m] = *reinterpret_cast<const bf16x8_t*>(ldsA(cur) + swz(arow_base + m * 32, c));
+          af[buf][m] = *reinterpret_cast<const bf16x8_t*>(
+              As + lds_off<C::kRowA>(arow_base + m * 32, cA));
+        if constexpr (kFP8) {
+          if ((s & 1) == 0) {
+#pragma unroll
+            for (int n = 0; n < NB; ++n)
+              raw8[n] = *reinterpret_cast<const u32x4_t*>(
+                  Bs + lds_off<C::kRowB>(brow(n), 2 * (s >> 1) + g));
+          }
+        } else {
+#pragma unroll
+          for (int n = 0; n < NB; ++n)
+            bf[buf][n] = *reinterpret_cast<const bf16x8_t*>(
+                Bs + lds_off<C::kRowB>(brow(n), 2 * s + g));
+        }
+      };
+      read_frags(0, 0);
+#pragma unroll
+      for (int s = 0; s < C::kSteps; ++s) {
+        const int cur = s & 1;
+        bf16x8_t b8[kFP8 ? NB : 1];
+        if constexpr (kFP8) {
+#pragma unroll
+          for (int n = 0; n < NB; ++n) {
+            const u32x2_t lo = e4m3x4_to_bf16x4(raw8[n][(s & 1) * 2]);
+            const u32x2_t hi = e4m3x4_to_bf16x4(raw8[n][(s & 1) * 2 + 1]);
+            b8[n] = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
+          }
+        }
+        if (s + 1 < C::kSteps) read_frags(s + 1, cur ^ 1);
 #pragma unroll
         for (int n = 0; n < NB; ++n) {
-          const bf16x8_t bfr = *reinterpret_cast<const bf16x8_t*>(ldsB(cur) + swz(brow(n), c));
+          const bf16x8_t bfr = kFP8 ? b8[n] : bf[cur][kFP8 ? 0 : n];
 #pragma unroll
           for (int m = 0; m < MB; ++m) {
+            // weights as the MFMA A operand: the result block is [feature][token]
             if constexpr (kFP8)
-              part[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[m], bfr, part[m][n], 0, 0, 0);
+              part[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr, af[cur][m], part[m][n], 0, 0, 0);
             else
-              acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[m], bfr, acc[m][n], 0, 0, 0);
+              acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr, af[cur][m], acc[m][n], 0, 0, 0);
           }
         }
       }
       if constexpr (kFP8) {
-        if (ks & 1) {  // end of a 128-deep scale block
-          const int kb = ks >> 1;
-          const int kblocks = a.K / 128;
+        if ((ks + 1) % (128 / kBK) == 0) {  // end of a 128-deep scale block
+          const int kb = (ks * kBK) / 128;
           float sc[NB];
 #pragma unroll
           for (int n = 0; n < NB; ++n) {
-            int nrow;  // first matrix row of the block -> its 128-row scale block
-            const float* S;
-            if (kGateUp) {
-              constexpr int H = NB / 2;
-              nrow = n0 + wn * H * 32 + (n % H) * 32;
-              S = n < H ? a.S0 : a.S1;
-            } else {
-              nrow = min(n0 + wn * NB * 32 + n * 32, a.Nout - 1);
-              S = a.S0;
-            }
-            sc[n] = S[((long long)j * (a.Nout / 128) + nrow / 128) * kblocks + kb];
+            const int sb = kGateUp ? (n < H ? 0 : 1) : (wn * NB * 32 + n * 32) / 128;
+            sc[n] = sc_lds[sb * C::kMaxKBlocks + kb];
           }
 #pragma unroll
           for (int m = 0; m < MB; ++m)
@@ -267,42 +359,51 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
             }
         }
       }
-      if (ks + 1 < nK) MOE_LSTORE(cur ^ 1);
-      __syncthreads();
     }
+#undef MOE_ISSUE_STAGE
 
-    // ---- epilogue (MFMA 32x32 layout: lane l holds column l % 32 and rows
-    // 8 (i / 4) + 4 (l / 32) + (i % 4) of each block)
+    // ---- epilogue.  Each result block is [feature][token] (MFMA 32x32 layout:
+    // lane l holds token column l % 32 and features 8 (q / 4) + 4 (l / 32) +
+    // (q % 4) for register q), so a lane owns runs of 4 consecutive features
+    // of one token row: one 8-byte store per run.
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = wm * MB * 32 + m * 32 + 8 * (i >> 2) + 4 * (l >> 5) + (i & 3);
-        const int p = row0 + r;
-        if (p >= row_end) continue;
+      const int p = row0 + wm * MB * 32 + m * 32 + (l & 31);
+      if (p < row_end) {
+        uint16_t* orow = a.out + (long long)p * a.Nout;
         if constexpr (kGateUp) {
-          constexpr int H = NB / 2;
 #pragma unroll
           for (int n = 0; n < H; ++n) {
-            const int col = n0 + wn * H * 32 + n * 32 + (l & 31);
-            const float gv = acc[m][n][i], uv = acc[m][n + H][i];
-            a.out[(long long)p * a.Nout + col] = f32_to_bf16(silu_f32(gv) * uv);
+#pragma unroll
+            for (int q = 0; q < 16; q += 4) {
+              const int col = n0 + wn * H * 32 + n * 32 + 8 * (q >> 2) + 4 * (l >> 5);
+              if (col < a.Nout) {
+                float h[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) h[u] = silu_f32(acc[m][n][q + u]) * acc[m][n + H][q + u];
+                *reinterpret_cast<u32x2_t*>(orow + col) =
+                    u32x2_t{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+              }
+            }
           }
         } else {
           const float gw = a.topk_w ? a.topk_w[a.sorted_slot[p]] : 1.0f;
 #pragma unroll
           for (int n = 0; n < NB; ++n) {
-            const int col = n0 + wn * NB * 32 + n * 32 + (l & 31);
-            if (col < a.Nout) a.out[(long long)p * a.Nout + col] = f32_to_bf16(acc[m][n][i] * gw);
+#pragma unroll
+            for (int q = 0; q < 16; q += 4) {
+              const int col = n0 + wn * NB * 32 + n * 32 + 8 * (q >> 2) + 4 * (l >> 5);
+              if (col < a.Nout)
+                *reinterpret_cast<u32x2_t*>(orow + col) =
+                    u32x2_t{pack_bf16x2(acc[m][n][q] * gw, acc[m][n][q + 1] * gw),
+                            pack_bf16x2(acc[m][n][q + 2] * gw, acc[m][n][q + 3] * gw)};
+            }
           }
         }
       }
     }
   }
 }
-
-#undef MOE_GLOAD
-#undef MOE_LSTORE
 
 // ---- float32 path: plain VALU dot products over the same tile schedule
 constexpr int kF32BM = 32;
@@ -362,10 +463,11 @@ int num_cu() {
   return g_num_cu;
 }
 
-template <int MB, int WM, int NB, int WN, bool kGateUp, bool kFP8, int kMinBlocks>
+template <int MB, int WM, int NB, int WN, bool kGateUp, bool kFP8, int kBK, int kStages,
+          int kMinBlocks>
 hipError_t launch_gemm(const GemmArgs& a, long long max_items, hipStream_t st) {
-  using C = Cfg<MB, WM, NB, WN, kGateUp, kFP8>;
-  auto kern = grouped_gemm_kernel<MB, WM, NB, WN, kGateUp, kFP8, kMinBlocks>;
+  using C = Cfg<MB, WM, NB, WN, kGateUp, kFP8, kBK, kStages>;
+  auto kern = grouped_gemm_kernel<MB, WM, NB, WN, kGateUp, kFP8, kBK, kStages, kMinBlocks>;
   static bool attr = false;
   if (!attr) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -382,15 +484,31 @@ hipError_t launch_gemm(const GemmArgs& a, long long max_items, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Tile shapes: decode (few rows per expert) and prefill (many rows).
-constexpr int kDecodeBM = 32;    // MB=1, WM=1
-constexpr int kPrefillBM = 128;  // MB=2, WM=2
+// Tile plans.  Decode (a handful of rows per expert): 32 x 256 tiles, four
+// waves side by side along N, 64-deep K steps, 4 stages.  bf16 prefill: eight
+// waves of 64 x 128, 32-deep K steps and 4 stages, as 128 x 512 tiles when
+// experts hold a few hundred rows (less M padding) or 256 x 256 when they hold
+// a thousand or more (fewer bytes staged per MFMA).  FP8 weights: four waves
+// (each keeps a second accumulator set for the per-block scales), 128 x 256
+// tiles, 64-deep K steps and 4 stages.
+enum class Plan { kF32, kDecode, kWide, kBig, kFp8 };
 
-bool use_decode_tiles(const Shape& s) { return s.S <= 64LL * s.El; }
+Plan plan_of(const Shape& s) {
+  if (s.weight == kF32) return Plan::kF32;
+  if (s.S <= 64LL * s.El) return Plan::kDecode;
+  if (s.weight == kFP8) return Plan::kFp8;
+  return s.S >= 1024LL * s.El ? Plan::kBig : Plan::kWide;
+}
+
+bool use_decode_tiles(const Shape& s) { return plan_of(s) == Plan::kDecode; }
 
 int tile_bm(const Shape& s) {
-  if (s.weight == kF32) return kF32BM;
-  return use_decode_tiles(s) ? kDecodeBM : kPrefillBM;
+  switch (plan_of(s)) {
+    case Plan::kF32: return kF32BM;
+    case Plan::kDecode: return 32;
+    case Plan::kBig: return 256;
+    default: return 128;
+  }
 }
 
 size_t max_tiles(const Shape& s, int bm) { return (size_t)((s.S + bm - 1) / bm) + s.El; }
@@ -462,6 +580,9 @@ hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
   dn.Nout = s.d;
 
   const long long mt = (long long)max_tiles(s, bm);
+  // decode tiles (about one M tile per expert) gain nothing from grouping and
+  // stream best in plain M-major order; prefill tiles group 8 M tiles
+  gu.group_m = dn.group_m = use_decode_tiles(s) ? 1 : 8;
   if (s.weight == kF32) {
     gu.n_tiles_n = (s.F + kF32BN - 1) / kF32BN;
     dn.n_tiles_n = (s.d + kF32BN - 1) / kF32BN;
@@ -476,32 +597,44 @@ hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
     return e;
   }
   const bool fp8 = s.weight == kFP8;
-  if (use_decode_tiles(s)) {
-    // 32 rows x 256 weight rows, 4 waves side by side along N
-    gu.n_tiles_n = s.F / 128;
-    dn.n_tiles_n = (s.d + 255) / 256;
-    if (fp8) {
-      e = launch_gemm<1, 1, 2, 4, true, true, 2>(gu, mt * gu.n_tiles_n, st);
+  auto ntn = [](int cols, int per_tile) { return (cols + per_tile - 1) / per_tile; };
+  switch (plan_of(s)) {
+    case Plan::kDecode:
+      gu.n_tiles_n = ntn(s.F, 128);
+      dn.n_tiles_n = ntn(s.d, 256);
+      if (fp8) {
+        e = launch_gemm<1, 1, 2, 4, true, true, 64, 4, 2>(gu, mt * gu.n_tiles_n, st);
+        if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
+        if (e == hipSuccess) e = launch_gemm<1, 1, 2, 4, false, true, 64, 4, 2>(dn, mt * dn.n_tiles_n, st);
+      } else {
+        e = launch_gemm<1, 1, 2, 4, true, false, 64, 4, 1>(gu, mt * gu.n_tiles_n, st);
+        if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
+        if (e == hipSuccess) e = launch_gemm<1, 1, 2, 4, false, false, 64, 4, 1>(dn, mt * dn.n_tiles_n, st);
+      }
+      break;
+    case Plan::kFp8:
+      gu.n_tiles_n = ntn(s.F, 128);
+      dn.n_tiles_n = ntn(s.d, 256);
+      e = launch_gemm<2, 2, 4, 2, true, true, 64, 4, 1>(gu, mt * gu.n_tiles_n, st);
       if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-      if (e == hipSuccess) e = launch_gemm<1, 1, 2, 4, false, true, 2>(dn, mt * dn.n_tiles_n, st);
-    } else {
-      e = launch_gemm<1, 1, 2, 4, true, false, 2>(gu, mt * gu.n_tiles_n, st);
+      if (e == hipSuccess) e = launch_gemm<2, 2, 4, 2, false, true, 64, 4, 1>(dn, mt * dn.n_tiles_n, st);
+      break;
+    case Plan::kWide:
+      gu.n_tiles_n = ntn(s.F, 256);
+      dn.n_tiles_n = ntn(s.d, 512);
+      e = launch_gemm<2, 2, 4, 4, true, false, 32, 4, 1>(gu, mt * gu.n_tiles_n, st);
       if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-      if (e == hipSuccess) e = launch_gemm<1, 1, 2, 4, false, false, 2>(dn, mt * dn.n_tiles_n, st);
-    }
-  } else {
-    // 128 rows x 256 weight rows, 2 x 2 waves of 64 x 128
-    gu.n_tiles_n = s.F / 128;
-    dn.n_tiles_n = (s.d + 255) / 256;
-    if (fp8) {
-      e = launch_gemm<2, 2, 4, 2, true, true, 1>(gu, mt * gu.n_tiles_n, st);
+      if (e == hipSuccess) e = launch_gemm<2, 2, 4, 4, false, false, 32, 4, 1>(dn, mt * dn.n_tiles_n, st);
+      break;
+    case Plan::kBig:
+      gu.n_tiles_n = ntn(s.F, 128);
+      dn.n_tiles_n = ntn(s.d, 256);
+      e = launch_gemm<2, 4, 4, 2, true, false, 32, 4, 1>(gu, mt * gu.n_tiles_n, st);
       if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-      if (e == hipSuccess) e = launch_gemm<2, 2, 4, 2, false, true, 1>(dn, mt * dn.n_tiles_n, st);
-    } else {
-      e = launch_gemm<2, 2, 4, 2, true, false, 1>(gu, mt * gu.n_tiles_n, st);
-      if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-      if (e == hipSuccess) e = launch_gemm<2, 2, 4, 2, false, false, 1>(dn, mt * dn.n_tiles_n, st);
-    }
+      if (e == hipSuccess) e = launch_gemm<2, 4, 4, 2, false, false, 32, 4, 1>(dn, mt * dn.n_tiles_n, st);
+      break;
+    case Plan::kF32:
+      break;
   }
   if (e == hipSuccess && ev) e = hipEventRecord(ev[2], st);
   return e;

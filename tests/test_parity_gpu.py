@@ -140,6 +140,10 @@ SMALL = {
     "fp8_many_slots_rank": synth.WORKLOADS["dsv3_rank"].replace(
         name="fp8_T2500_d256_E64_local48-63_k6_F256", T=2500, d=256, E=64, num_local=16,
         expert_begin=48, k=6, F=256, seed=28),
+    # >= 1024 rows per expert: 256 x 256 tiles, N tiles clipped in both GEMMs
+    "bf16_big_tiles": synth.WORKLOADS["mixtral"].replace(
+        name="bf16_T2100_d384_E4_k2_F384_gauss", T=2100, d=384, E=4, num_local=4, k=2, F=384,
+        seed=29),
     # f32 with more tiles than the tiny workload
     "f32_tiles": synth.WORKLOADS["tiny"].replace(
         name="f32_T300_d256_E8_k3_F384", T=300, d=256, E=8, num_local=8, k=3, F=384, seed=26),
