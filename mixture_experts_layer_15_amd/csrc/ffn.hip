@@ -101,6 +101,24 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Scheduling hint for one MFMA step: kReads LDS reads alternating with the
+// first kReads of the step's kMfma MFMAs, then the remaining MFMAs.
+template <int kReads, int kMfma>
+__device__ __forceinline__ void sched_alternate() {
+  constexpr int kPairs = kReads < kMfma ? kReads : kMfma;
+#pragma unroll
+  for (int q = 0; q < kPairs; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+  }
+  if constexpr (kMfma > kPairs) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kPairs, 0);
+  if constexpr (kReads > kPairs) __builtin_amdgcn_sched_group_barrier(0x100, kReads - kPairs, 0);
+}
+
+// s_waitcnt lgkmcnt(0): this wave's LDS reads have returned (vmcnt and
+// expcnt left alone).
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // Workgroup barrier without a memory fence.  LDS-DMA data of a stage is in
 // LDS once the issuing wave's vmcnt wait returns, and LDS executes each
 // wave's operations in order; the empty asm statements keep the compiler from
@@ -148,11 +166,13 @@ struct Cfg {
   static_assert(kBK == 32 || kBK == 64, "K step");
   static_assert(kStageA % (1024 * kWaves) == 0 && kStageB % (1024 * kWaves) == 0, "load split");
   static_assert(!kGateUp || NB % 2 == 0, "gate/up pairs column blocks");
-  static_assert(kStages >= 2 && (kStages - 2) * kLoads < 64, "vmcnt budget");
+  static_assert(kStages >= 2 && (kStages - 1) * kLoads < 64, "vmcnt budget");
   static_assert(kLds <= 160 * 1024, "LDS budget");
   static_assert(128 % kBK == 0, "a scale block spans whole K steps");
   static_assert(!kFP8 || !kGateUp || BNW / 2 == 128, "gate/up scales: one 128-row block");
   static_assert(!kFP8 || BNW % 128 == 0, "down scales: whole 128-row blocks");
+  static_assert(!kFP8 || kBK == 64, "FP8 raw codes are double-buffered per step pair");
+  static_assert(kSteps % 2 == 0, "fragment buffers alternate by step");
 };
 
 template <int MB, int WM, int NB, int WN, bool kGateUp, bool kFP8, int kBK, int kStages,
@@ -273,72 +293,102 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
         for (int n = 0; n < NB; ++n) part[m][n] = f32x16_t{};
     }
 
-#pragma unroll
-    for (int st = 0; st < kStages - 1; ++st)
-      if (st < nK) MOE_ISSUE_STAGE(st);
-
-    for (int ks = 0; ks < nK; ++ks) {
-      // stage ks has landed once only the later stages' loads remain in flight
-      if (ks + kStages - 2 < nK)
-        wait_vmcnt<(kStages - 2) * C::kLoads>();
-      else
-        wait_vmcnt<0>();
-      stage_barrier();  // all waves' loads of stage ks landed; stage ks-1 is free
-      if (ks + kStages - 1 < nK) MOE_ISSUE_STAGE(ks + kStages - 1);
-
-      const unsigned char* As = smem + (ks % kStages) * C::kStage;
+    // MFMA operand fragments of one K step (tokens: A; weights: B; FP8
+    // weights as raw codes for a pair of steps, widened at use).  K
+    // permutation shared by both operands: bf16 weights use chunk 2s + g at
+    // step s; an FP8 lane holds one 16-byte chunk (16 K values) for steps
+    // 2p and 2p + 1.
+    bf16x8_t af[2][MB];
+    bf16x8_t bf[2][kFP8 ? 1 : NB];
+    u32x4_t raw8[2][kFP8 ? NB : 1];
+    auto read_frags = [&](int stage, int s, int buf) {
+      const unsigned char* As = smem + (stage % kStages) * C::kStage;
       const unsigned char* Bs = As + C::kStageA;
-      // K permutation shared by A and B: bf16 weights use chunk 2s + g at step
-      // s; FP8 weights give each lane one 16-byte chunk (16 K values) for two
-      // steps.  Fragments of step s + 1 are read before step s's MFMAs issue.
-      bf16x8_t af[2][MB];
-      bf16x8_t bf[2][kFP8 ? 1 : NB];
-      u32x4_t raw8[kFP8 ? NB : 1];
-      auto read_frags = [&](int s, int buf) {
-        const int cA = kFP8 ? (4 * (s >> 1) + 2 * g + (s & 1)) : (2 * s + g);
+      const int cA = kFP8 ? (4 * (s >> 1) + 2 * g + (s & 1)) : (2 * s + g);
 #pragma unroll
-        for (int m = 0; m < MB; ++m)
-          af[buf][m] = *reinterpret_cast<const bf16x8_t*>(
-              As + lds_off<C::kRowA>(arow_base + m * 32, cA));
-        if constexpr (kFP8) {
-          if ((s & 1) == 0) {
-#pragma unroll
-            for (int n = 0; n < NB; ++n)
-              raw8[n] = *reinterpret_cast<const u32x4_t*>(
-                  Bs + lds_off<C::kRowB>(brow(n), 2 * (s >> 1) + g));
-          }
-        } else {
+      for (int m = 0; m < MB; ++m)
+        af[buf][m] = *reinterpret_cast<const bf16x8_t*>(
+            As + lds_off<C::kRowA>(arow_base + m * 32, cA));
+      if constexpr (kFP8) {
+        if ((s & 1) == 0) {
 #pragma unroll
           for (int n = 0; n < NB; ++n)
-            bf[buf][n] = *reinterpret_cast<const bf16x8_t*>(
-                Bs + lds_off<C::kRowB>(brow(n), 2 * s + g));
+            raw8[(s >> 1) & 1][n] = *reinterpret_cast<const u32x4_t*>(
+                Bs + lds_off<C::kRowB>(brow(n), 2 * (s >> 1) + g));
         }
-      };
-      read_frags(0, 0);
+      } else {
+#pragma unroll
+        for (int n = 0; n < NB; ++n)
+          bf[buf][n] = *reinterpret_cast<const bf16x8_t*>(
+              Bs + lds_off<C::kRowB>(brow(n), 2 * s + g));
+      }
+    };
+    auto mfma_step = [&](int s, int buf) {
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+        bf16x8_t bfr;
+        if constexpr (kFP8) {
+          const u32x4_t r = raw8[(s >> 1) & 1][n];
+          const u32x2_t lo = e4m3x4_to_bf16x4(r[(s & 1) * 2]);
+          const u32x2_t hi = e4m3x4_to_bf16x4(r[(s & 1) * 2 + 1]);
+          bfr = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
+        } else {
+          bfr = bf[buf][n];
+        }
+#pragma unroll
+        for (int m = 0; m < MB; ++m) {
+          // weights as the MFMA A operand: the result block is [feature][token]
+          if constexpr (kFP8)
+            part[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr, af[buf][m], part[m][n], 0, 0, 0);
+          else
+            acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr, af[buf][m], acc[m][n], 0, 0, 0);
+        }
+      }
+    };
+
+    // prologue: all stages in flight, stage 0 landed, its first fragments read
+#pragma unroll
+    for (int st = 0; st < kStages; ++st)
+      if (st < nK) MOE_ISSUE_STAGE(st);
+    if (nK >= kStages)
+      wait_vmcnt<(kStages - 1) * C::kLoads>();
+    else
+      wait_vmcnt<0>();
+    stage_barrier();
+    read_frags(0, 0, 0);
+
+    // Steady state.  The barrier for stage ks + 1 sits between the last two
+    // MFMA steps of stage ks: waves wait at it while their earlier MFMAs still
+    // occupy the matrix pipe, then refill the freed buffer of stage ks with
+    // stage ks + kStages and read stage ks + 1's first fragments while the
+    // last step's MFMAs run.
+    for (int ks = 0; ks < nK; ++ks) {
 #pragma unroll
       for (int s = 0; s < C::kSteps; ++s) {
-        const int cur = s & 1;
-        bf16x8_t b8[kFP8 ? NB : 1];
-        if constexpr (kFP8) {
-#pragma unroll
-          for (int n = 0; n < NB; ++n) {
-            const u32x2_t lo = e4m3x4_to_bf16x4(raw8[n][(s & 1) * 2]);
-            const u32x2_t hi = e4m3x4_to_bf16x4(raw8[n][(s & 1) * 2 + 1]);
-            b8[n] = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
-          }
-        }
-        if (s + 1 < C::kSteps) read_frags(s + 1, cur ^ 1);
-#pragma unroll
-        for (int n = 0; n < NB; ++n) {
-          const bf16x8_t bfr = kFP8 ? b8[n] : bf[cur][kFP8 ? 0 : n];
-#pragma unroll
-          for (int m = 0; m < MB; ++m) {
-            // weights as the MFMA A operand: the result block is [feature][token]
-            if constexpr (kFP8)
-              part[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr, af[cur][m], part[m][n], 0, 0, 0);
+        if (s + 1 < C::kSteps) {
+          read_frags(ks, s + 1, (s + 1) & 1);
+          mfma_step(s, s & 1);
+          // alternate MFMA and LDS read (the next step's fragments): bursts of
+          // reads stall the issuing waves, alternating keeps the matrix pipe fed
+          if (kFP8 && (s + 1) % 2 != 0)  // FP8 weights are read every other step
+            sched_alternate<MB, MB * NB>();
+          else
+            sched_alternate<MB + NB, MB * NB>();
+        } else {
+          __builtin_amdgcn_sched_barrier(0);
+          wait_lgkmcnt0();  // this wave's reads of stage ks have returned
+          if (ks + 1 < nK) {
+            if (ks + kStages - 1 < nK)
+              wait_vmcnt<(kStages - 2) * C::kLoads>();  // stage ks + 1 landed
             else
-              acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr, af[cur][m], acc[m][n], 0, 0, 0);
+              wait_vmcnt<0>();
           }
+          stage_barrier();  // stage ks + 1 visible; nobody reads stage ks any more
+          if (ks + kStages < nK) MOE_ISSUE_STAGE(ks + kStages);
+          __builtin_amdgcn_sched_barrier(0);
+          if (ks + 1 < nK) read_frags(ks + 1, 0, 0);
+          mfma_step(s, s & 1);
+          if (ks + 1 < nK) sched_alternate<MB + NB, MB * NB>();
         }
       }
       if constexpr (kFP8) {

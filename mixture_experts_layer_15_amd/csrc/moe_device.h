@@ -48,6 +48,10 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+// silu(z) = z * sigmoid(z) with the hardware exp2 and reciprocal (about 1 ulp
+// each; the bf16/fp8 paths round h to bf16 right after).
+__device__ __forceinline__ float silu_f32(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 }  // namespace moe
