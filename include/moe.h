@@ -37,6 +37,9 @@
  *    is re-entrant.  Scratch memory comes from the caller (moe_workspace_size).
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Every call only enqueues kernels on it and returns.
+ *  - The environment variable MOE_MI355X_MAX_WORKGROUPS, if set to a positive
+ *    number, caps the workgroups of the persistent expert GEMM kernels (a
+ *    test aid; results are the same for every value).
  *  - A slot is s = t*k + i (token t, its i-th chosen expert).  Expert ids in
  *    index arrays are global ids in [0, E).
  *  - Formats: activations and the router matrix are MOE_F32 or MOE_BF16;

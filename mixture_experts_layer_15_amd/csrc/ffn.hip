@@ -27,6 +27,8 @@
 //    sum times its block's scale, so the weights enter MFMA unrounded;
 //  * epilogues: silu(gate) * up rounded to bf16 (gate/up), or the product
 //    times the token's gate (down).
+#include <stdlib.h>
+
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -36,7 +38,7 @@ namespace {
 constexpr int kNumXcd = 8;
 
 __global__ __launch_bounds__(kMaxExperts) void ffn_schedule_kernel(const int32_t* offsets, int El,
-                                                                   int BM, int2* tiles,
+                                                                   int BM, int4* tiles,
                                                                    int* ntiles) {
   __shared__ int sums[kMaxExperts];
   const int e = threadIdx.x;
@@ -52,7 +54,7 @@ __global__ __launch_bounds__(kMaxExperts) void ffn_schedule_kernel(const int32_t
     __syncthreads();
   }
   const int first = sums[e] - nt;
-  for (int i = 0; i < nt; ++i) tiles[first + i] = make_int2(e, lo + i * BM);
+  for (int i = 0; i < nt; ++i) tiles[first + i] = make_int4(e, lo + i * BM, lo + cnt, 0);
   if (e == El - 1) *ntiles = sums[e];
 }
 
@@ -67,7 +69,7 @@ struct GemmArgs {
   const float* topk_w;         // down epilogue gates, or null
   uint16_t* out;               // gate/up: h [S][Nout]; down: y [S][Nout]
   const int32_t* offsets;      // [El + 1]
-  const int2* tiles;           // (expert, row0)
+  const int4* tiles;           // (expert, first row, expert's end row, 0)
   const int* ntiles;
   int K;                       // reduction length
   int Nout;                    // output columns
@@ -143,6 +145,17 @@ __device__ __forceinline__ void lds_dma16(const void* src, unsigned char* lds) {
 #endif
 }
 
+// One 4-byte global -> LDS load per active lane (global_load_lds_dword): lane
+// i's value lands at lds + 4 i.
+__device__ __forceinline__ void lds_dma4(const void* src, unsigned char* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+#else
+  (void)src;
+  (void)lds;
+#endif
+}
+
 template <int MB, int WM, int NB, int WN, bool kGateUp, bool kFP8, int kBK, int kStages>
 struct Cfg {
   static constexpr int kWaves = WM * WN;
@@ -162,7 +175,7 @@ struct Cfg {
   static constexpr int kSteps = kBK / 16;                     // MFMA K steps per stage
   static constexpr int kScaleSets = kFP8 ? (kGateUp ? 2 : BNW / 128) : 0;
   static constexpr int kMaxKBlocks = 65536 / 128;
-  static constexpr int kLds = kStages * kStage + kScaleSets * kMaxKBlocks * 4;
+  static constexpr int kLds = kStages * kStage + 2 * kScaleSets * kMaxKBlocks * 4;
   static_assert(kBK == 32 || kBK == 64, "K step");
   static_assert(kStageA % (1024 * kWaves) == 0 && kStageB % (1024 * kWaves) == 0, "load split");
   static_assert(!kGateUp || NB % 2 == 0, "gate/up pairs column blocks");
@@ -182,6 +195,8 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
   constexpr int BNW = C::BNW;
   constexpr int H = NB / 2;  // gate/up: column blocks per half
   extern __shared__ __align__(16) unsigned char smem[];
+  // LDS: kStages pipeline stages | FP8 block scales of two items (the running
+  // one and the next), [sets][KB] each
   float* sc_lds = reinterpret_cast<float*>(smem + kStages * C::kStage);
 
   const int tid = threadIdx.x;
@@ -193,53 +208,87 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
   const int welem = kFP8 ? 1 : 2;  // bytes per weight element
   const int nK = a.K / kBK;
   const int KB = a.K / 128;
+  const int n_sc = C::kScaleSets * KB;  // scale floats per item
 
   // persistent, XCD-contiguous item ranges
-  const int n_items = *a.ntiles * a.n_tiles_n;
+  const int n_mtiles = *a.ntiles;
+  const int n_items = n_mtiles * a.n_tiles_n;
   const int xcd = blockIdx.x % kNumXcd;
   const int per_xcd = gridDim.x / kNumXcd;
   const int slot = blockIdx.x / kNumXcd;
   const int it_begin = (int)((long long)n_items * xcd / kNumXcd);
   const int it_end = (int)((long long)n_items * (xcd + 1) / kNumXcd);
+  const int per_group = a.group_m * a.n_tiles_n;
 
-  // weight-tile row of this lane's MFMA column in block n
+  // item -> (M tile, first output column).  Grouped order: items run through
+  // groups of group_m consecutive M tiles, M fastest inside a group, so the
+  // workgroups of an XCD that run at the same time share a few A tiles and a
+  // few weight tiles in L2 (instead of one A tile and as many weight tiles as
+  // workgroups).
+  auto place = [&](int item) -> int2 {
+    const int grp = item / per_group;
+    const int first_m = grp * a.group_m;
+    const int gsize = min(a.group_m, n_mtiles - first_m);
+    const int in_grp = item - grp * per_group;
+    return make_int2(first_m + in_grp % gsize, (in_grp / gsize) * (kGateUp ? BNW / 2 : BNW));
+  };
+
+  // Weight rows enter each 32-row MFMA block permuted: block row 8a + 4g + b
+  // (a, b < 4; g < 2) holds feature 16g + 4a + b, so that a lane's 16 result
+  // registers are 16 consecutive output features (see the epilogue).
+  auto feat_of_row = [](int r) -> int {
+    return (r & ~31) | (((r >> 2) & 1) << 4) | (((r >> 3) & 3) << 2) | (r & 3);
+  };
+  // LDS row of this lane's MFMA operand in weight block n (A operand of MFMA)
   auto brow = [&](int n) -> int {
     if (kGateUp) return (n < H ? 0 : BNW / 2) + wn * H * 32 + (n % H) * 32 + (l & 31);
     return wn * NB * 32 + n * 32 + (l & 31);
   };
   const int arow_base = wm * MB * 32 + (l & 31);
 
-  const int n_mtiles = *a.ntiles;
-  for (int item = it_begin + slot; item < it_end; item += per_xcd) {
-    // grouped order: items run through groups of group_m consecutive M tiles,
-    // M fastest inside a group, so the workgroups of an XCD that run at the
-    // same time share a few A tiles and a few weight tiles in L2 (instead of
-    // one A tile and as many weight tiles as workgroups)
-    const int per_group = a.group_m * a.n_tiles_n;
-    const int grp = item / per_group;
-    const int first_m = grp * a.group_m;
-    const int gsize = min(a.group_m, n_mtiles - first_m);
-    const int in_grp = item - grp * per_group;
-    const int gt = first_m + in_grp % gsize;
-    const int nt = in_grp / gsize;
-    const int2 tile = a.tiles[gt];
-    const int j = tile.x;
-    const int row0 = tile.y;
-    const int row_end = a.offsets[j + 1];
-    const int n0 = nt * (kGateUp ? BNW / 2 : BNW);  // first output column of the tile
+  // rows: gate/up: sorted_slot of the A row of each of this lane's LDS-DMA
+  // chunks; down: sorted_slot of this lane's epilogue rows (for the gates)
+  constexpr int kRows = kGateUp ? C::kLoadsA : MB;
+  auto load_rows = [&](int row0, int row_end, int* rows) {
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+      if (kGateUp) {
+        const int P = (wave * C::kLoadsA + i) * kWave + l;
+        rows[i] = a.sorted_slot[min(row0 + P / C::kChunksA, row_end - 1)];
+      } else {
+        const int p = row0 + arow_base + i * 32;
+        rows[i] = p < row_end ? a.sorted_slot[p] : 0;
+      }
+    }
+  };
+  // FP8: an item's block scales go straight to LDS (LDS-DMA, 64 floats per
+  // wave instruction), into the scale buffer the item will read
+  auto dma_scales = [&](int j, int n0, int buf) {
+    for (int c0 = wave * kWave; c0 < n_sc; c0 += C::kThreads) {
+      const int o = c0 + l;
+      if (o < n_sc) {
+        const int sb = o / KB, kb = o % KB;
+        const float* S = (kGateUp && sb == 1) ? a.S1 : a.S0;
+        const int nblk = min(kGateUp ? n0 / 128 : n0 / 128 + sb, a.Nout / 128 - 1);
+        lds_dma4(S + ((long long)j * (a.Nout / 128) + nblk) * KB + kb,
+                 reinterpret_cast<unsigned char*>(sc_lds + buf * n_sc + c0));
+      }
+    }
+  };
 
-    // ---- this lane's source chunk of every LDS-DMA load of a stage (step 0)
-    const unsigned char* srcA[C::kLoadsA];
+  // this lane's source chunk of every LDS-DMA load of an item's stage 0
+  const unsigned char* srcA[C::kLoadsA];
+  const unsigned char* srcB[C::kLoadsB];
+  auto set_src = [&](int j, int row0, int row_end, int n0, const int* rows) {
 #pragma unroll
     for (int i = 0; i < C::kLoadsA; ++i) {
       const int P = (wave * C::kLoadsA + i) * kWave + l;  // 16-byte chunk position
       const int r = P / C::kChunksA;
       const int c = (P % C::kChunksA) ^ ((r / (256 / C::kRowA)) % C::kChunksA);
-      const int p = min(row0 + r, row_end - 1);
-      const long long arow = kGateUp ? (long long)(a.sorted_slot[p] / a.k) : (long long)p;
+      const long long arow = kGateUp ? (long long)(rows[kGateUp ? i : 0] / a.k)
+                                     : (long long)min(row0 + r, row_end - 1);
       srcA[i] = reinterpret_cast<const unsigned char*>(a.A + arow * a.K) + c * 16;
     }
-    const unsigned char* srcB[C::kLoadsB];
 #pragma unroll
     for (int i = 0; i < C::kLoadsB; ++i) {
       const int P = (wave * C::kLoadsB + i) * kWave + l;
@@ -249,36 +298,128 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
       int wrow;
       if (kGateUp) {
         const bool up = r >= BNW / 2;
-        wrow = min(n0 + (up ? r - BNW / 2 : r), a.Nout - 1);
+        wrow = min(n0 + feat_of_row(up ? r - BNW / 2 : r), a.Nout - 1);
         base = static_cast<const unsigned char*>(up ? a.W1 : a.W0);
       } else {
-        wrow = min(n0 + r, a.Nout - 1);
+        wrow = min(n0 + feat_of_row(r), a.Nout - 1);
         base = static_cast<const unsigned char*>(a.W0);
       }
       srcB[i] = base + ((long long)j * a.Nout + wrow) * a.K * welem + c * 16;
     }
+  };
 
-    stage_barrier();  // every wave is done with the previous item's stages and scales
-    if constexpr (kFP8) {
-      // this tile's block scales -> LDS: set sb holds gate/up (gate/up GEMM) or
-      // the sb-th 128-row block of the tile (down GEMM), for every K block
-      for (int o = tid; o < C::kScaleSets * KB; o += C::kThreads) {
-        const int sb = o / KB, kb = o % KB;
-        const float* S = (kGateUp && sb == 1) ? a.S1 : a.S0;
-        const int nblk = min(kGateUp ? n0 / 128 : n0 / 128 + sb, a.Nout / 128 - 1);
-        sc_lds[sb * C::kMaxKBlocks + kb] = S[((long long)j * (a.Nout / 128) + nblk) * KB + kb];
-      }
-    }
-
-#define MOE_ISSUE_STAGE(KS)                                                                     \
+  // stage Q of the item srcA/srcB point at, into the buffer of pipeline stage G
+#define MOE_ISSUE_STAGE(Q, G)                                                                   \
   do {                                                                                          \
-    unsigned char* sb_ = smem + ((KS) % kStages) * C::kStage;                                   \
+    unsigned char* sb_ = smem + ((G) % kStages) * C::kStage;                                    \
     _Pragma("unroll") for (int i = 0; i < C::kLoadsA; ++i)                                      \
-        lds_dma16(srcA[i] + (long long)(KS) * kBK * 2, sb_ + (wave * C::kLoadsA + i) * 1024);   \
+        lds_dma16(srcA[i] + (long long)(Q) * kBK * 2, sb_ + (wave * C::kLoadsA + i) * 1024);    \
     _Pragma("unroll") for (int i = 0; i < C::kLoadsB; ++i)                                      \
-        lds_dma16(srcB[i] + (long long)(KS) * kBK * welem,                                      \
+        lds_dma16(srcB[i] + (long long)(Q) * kBK * welem,                                       \
                   sb_ + C::kStageA + (wave * C::kLoadsB + i) * 1024);                            \
   } while (0)
+
+  int item = it_begin + slot;
+  if (item >= it_end) return;
+
+  // tiles as (expert, first row, end row) and first output column of the
+  // running item (c), the next (x) and the one after it (y)
+  int cj, c0, ce, n0c, xj = 0, x0 = 0, xe = 1, n0x = 0;
+  {
+    const int2 pl = place(item);
+    const int4 t = a.tiles[pl.x];
+    cj = t.x, c0 = t.y, ce = t.z, n0c = pl.y;
+  }
+  if (item + per_xcd < it_end) {
+    const int2 pl = place(item + per_xcd);
+    const int4 t = a.tiles[pl.x];
+    xj = t.x, x0 = t.y, xe = t.z, n0x = pl.y;
+  }
+  int rows_cur[kRows];
+  load_rows(c0, ce, rows_cur);
+  // Every register load above has landed before the loop: the loop's own
+  // waits for them then fall on points where all earlier loads are known
+  // complete, and the compiler places no wait of its own inside the loop.
+  wait_vmcnt<0>();
+  if constexpr (kFP8) dma_scales(cj, n0c, 0);  // lands before stage 0 does
+  set_src(cj, c0, ce, n0c, rows_cur);
+#pragma unroll
+  for (int st = 0; st < kStages; ++st)
+    if (st < nK) MOE_ISSUE_STAGE(st, st);
+  // MFMA operand fragments of one K step (tokens: B operand; weights: A
+  // operand; FP8 weights as raw codes for a pair of steps, widened at use).
+  // K permutation shared by both operands: bf16 weights use chunk 2s + g at
+  // step s; an FP8 lane holds one 16-byte chunk (16 K values) for steps
+  // 2p and 2p + 1.
+  bf16x8_t af[2][MB];
+  bf16x8_t bf[2][kFP8 ? 1 : NB];
+  u32x4_t raw8[2][kFP8 ? NB : 1];
+  auto read_frags = [&](int stage, int s, int buf) {
+    const unsigned char* As = smem + (stage % kStages) * C::kStage;
+    const unsigned char* Bs = As + C::kStageA;
+    const int cA = kFP8 ? (4 * (s >> 1) + 2 * g + (s & 1)) : (2 * s + g);
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+      af[buf][m] = *reinterpret_cast<const bf16x8_t*>(
+          As + lds_off<C::kRowA>(arow_base + m * 32, cA));
+    if constexpr (kFP8) {
+      if ((s & 1) == 0) {
+#pragma unroll
+        for (int n = 0; n < NB; ++n)
+          raw8[(s >> 1) & 1][n] = *reinterpret_cast<const u32x4_t*>(
+              Bs + lds_off<C::kRowB>(brow(n), 2 * (s >> 1) + g));
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < NB; ++n)
+        bf[buf][n] = *reinterpret_cast<const bf16x8_t*>(
+            Bs + lds_off<C::kRowB>(brow(n), 2 * s + g));
+    }
+  };
+
+  int base = 0;    // pipeline stage number of this item's stage 0
+  int parity = 0;  // scale buffer of this item
+
+  for (;;) {
+    const int item_n = item + per_xcd;
+    const bool has_next = item_n < it_end;
+    const bool has_nn = item_n + per_xcd < it_end;
+
+    // this item's stage 0 has landed once only its later stages (and younger
+    // loads or stores) remain in flight
+    if (nK >= kStages)
+      wait_vmcnt<(kStages - 1) * C::kLoads>();
+    else
+      wait_vmcnt<0>();
+    stage_barrier();  // stage 0 and this item's scales are visible to all waves
+    read_frags(base, 0, 0);
+
+    // down: this item's gates, read in its epilogue
+    float gw[kGateUp ? 1 : MB];
+    if constexpr (!kGateUp) {
+#pragma unroll
+      for (int m = 0; m < MB; ++m)
+        gw[m] = (a.topk_w && c0 + arow_base + m * 32 < ce) ? a.topk_w[rows_cur[m]] : 1.0f;
+    }
+
+    // the next item's inputs and the tile of the item after it
+    int yj = xj, y0 = x0, ye = xe, n0y = n0x;
+    int rows_nxt[kRows];
+    if (has_nn) n0y = place(item_n + per_xcd).y;
+    if (has_next) {
+      load_rows(x0, xe, rows_nxt);
+      if (has_nn) {
+        // an index the compiler cannot prove wave-uniform keeps the tile in
+        // vector registers: moving a loaded value to scalar registers would
+        // wait for it (and for every stage load in flight) right here
+        int opaque_zero;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(opaque_zero));
+        const int4 t = a.tiles[place(item_n + per_xcd).x + opaque_zero];
+        yj = t.x, y0 = t.y, ye = t.z;
+      }
+      // the other scale buffer was last read by the previous item
+      if constexpr (kFP8) dma_scales(xj, n0x, parity ^ 1);
+    }
 
     f32x16_t acc[MB][NB];
     f32x16_t part[kFP8 ? MB : 1][kFP8 ? NB : 1];
@@ -293,36 +434,6 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
         for (int n = 0; n < NB; ++n) part[m][n] = f32x16_t{};
     }
 
-    // MFMA operand fragments of one K step (tokens: A; weights: B; FP8
-    // weights as raw codes for a pair of steps, widened at use).  K
-    // permutation shared by both operands: bf16 weights use chunk 2s + g at
-    // step s; an FP8 lane holds one 16-byte chunk (16 K values) for steps
-    // 2p and 2p + 1.
-    bf16x8_t af[2][MB];
-    bf16x8_t bf[2][kFP8 ? 1 : NB];
-    u32x4_t raw8[2][kFP8 ? NB : 1];
-    auto read_frags = [&](int stage, int s, int buf) {
-      const unsigned char* As = smem + (stage % kStages) * C::kStage;
-      const unsigned char* Bs = As + C::kStageA;
-      const int cA = kFP8 ? (4 * (s >> 1) + 2 * g + (s & 1)) : (2 * s + g);
-#pragma unroll
-      for (int m = 0; m < MB; ++m)
-        af[buf][m] = *reinterpret_cast<const bf16x8_t*>(
-            As + lds_off<C::kRowA>(arow_base + m * 32, cA));
-      if constexpr (kFP8) {
-        if ((s & 1) == 0) {
-#pragma unroll
-          for (int n = 0; n < NB; ++n)
-            raw8[(s >> 1) & 1][n] = *reinterpret_cast<const u32x4_t*>(
-                Bs + lds_off<C::kRowB>(brow(n), 2 * (s >> 1) + g));
-        }
-      } else {
-#pragma unroll
-        for (int n = 0; n < NB; ++n)
-          bf[buf][n] = *reinterpret_cast<const bf16x8_t*>(
-              Bs + lds_off<C::kRowB>(brow(n), 2 * s + g));
-      }
-    };
     auto mfma_step = [&](int s, int buf) {
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
@@ -346,19 +457,8 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
       }
     };
 
-    // prologue: all stages in flight, stage 0 landed, its first fragments read
-#pragma unroll
-    for (int st = 0; st < kStages; ++st)
-      if (st < nK) MOE_ISSUE_STAGE(st);
-    if (nK >= kStages)
-      wait_vmcnt<(kStages - 1) * C::kLoads>();
-    else
-      wait_vmcnt<0>();
-    stage_barrier();
-    read_frags(0, 0, 0);
-
-    // Steady state.  The barrier for stage ks + 1 sits between the last two
-    // MFMA steps of stage ks: waves wait at it while their earlier MFMAs still
+    // K loop.  The barrier for stage ks + 1 sits between the last two MFMA
+    // steps of stage ks: waves wait at it while their earlier MFMAs still
     // occupy the matrix pipe, then refill the freed buffer of stage ks with
     // stage ks + kStages and read stage ks + 1's first fragments while the
     // last step's MFMAs run.
@@ -366,7 +466,7 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
 #pragma unroll
       for (int s = 0; s < C::kSteps; ++s) {
         if (s + 1 < C::kSteps) {
-          read_frags(ks, s + 1, (s + 1) & 1);
+          read_frags(base + ks, s + 1, (s + 1) & 1);
           mfma_step(s, s & 1);
           // alternate MFMA and LDS read (the next step's fragments): bursts of
           // reads stall the issuing waves, alternating keeps the matrix pipe fed
@@ -375,20 +475,21 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
           else
             sched_alternate<MB + NB, MB * NB>();
         } else {
+          const bool more = ks + 1 < nK;
           __builtin_amdgcn_sched_barrier(0);
           wait_lgkmcnt0();  // this wave's reads of stage ks have returned
-          if (ks + 1 < nK) {
+          if (more) {
             if (ks + kStages - 1 < nK)
               wait_vmcnt<(kStages - 2) * C::kLoads>();  // stage ks + 1 landed
             else
               wait_vmcnt<0>();
           }
           stage_barrier();  // stage ks + 1 visible; nobody reads stage ks any more
-          if (ks + kStages < nK) MOE_ISSUE_STAGE(ks + kStages);
+          if (ks + kStages < nK) MOE_ISSUE_STAGE(ks + kStages, base + ks + kStages);
           __builtin_amdgcn_sched_barrier(0);
-          if (ks + 1 < nK) read_frags(ks + 1, 0, 0);
+          if (more) read_frags(base + ks + 1, 0, 0);
           mfma_step(s, s & 1);
-          if (ks + 1 < nK) sched_alternate<MB + NB, MB * NB>();
+          if (more) sched_alternate<MB + NB, MB * NB>();
         }
       }
       if constexpr (kFP8) {
@@ -398,7 +499,7 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
 #pragma unroll
           for (int n = 0; n < NB; ++n) {
             const int sb = kGateUp ? (n < H ? 0 : 1) : (wn * NB * 32 + n * 32) / 128;
-            sc[n] = sc_lds[sb * C::kMaxKBlocks + kb];
+            sc[n] = sc_lds[parity * n_sc + sb * KB + kb];
           }
 #pragma unroll
           for (int m = 0; m < MB; ++m)
@@ -410,49 +511,61 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
         }
       }
     }
-#undef MOE_ISSUE_STAGE
+
+    if (has_next) {
+      // The next item's first stages go out before this item's epilogue, so
+      // their latency overlaps it.  The wait covers every load issued so far
+      // (the next item's inputs among them); the barrier frees all stage
+      // buffers (and the other scale buffer).
+      wait_vmcnt<0>();
+      stage_barrier();
+      set_src(xj, x0, xe, n0x, rows_nxt);
+#pragma unroll
+      for (int st = 0; st < kStages; ++st)
+        if (st < nK) MOE_ISSUE_STAGE(st, base + nK + st);
+    } else {
+      wait_vmcnt<0>();  // the gates: nothing else is in flight any more
+    }
 
     // ---- epilogue.  Each result block is [feature][token] (MFMA 32x32 layout:
-    // lane l holds token column l % 32 and features 8 (q / 4) + 4 (l / 32) +
-    // (q % 4) for register q), so a lane owns runs of 4 consecutive features
-    // of one token row: one 8-byte store per run.
+    // lane l holds token column l % 32 in its 16 registers); with the weight-row
+    // permutation, register q is feature 16 (l / 32) + q of the block, so a
+    // lane stores 16 consecutive features of one token row: two 16-byte stores.
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
-      const int p = row0 + wm * MB * 32 + m * 32 + (l & 31);
-      if (p < row_end) {
+      const int p = c0 + arow_base + m * 32;
+      if (p < ce) {
         uint16_t* orow = a.out + (long long)p * a.Nout;
-        if constexpr (kGateUp) {
 #pragma unroll
-          for (int n = 0; n < H; ++n) {
+        for (int n = 0; n < (kGateUp ? H : NB); ++n) {
+          const int col = n0c + wn * (kGateUp ? H : NB) * 32 + n * 32 + 16 * g;
+          if (col < a.Nout) {
+            float h[16];
 #pragma unroll
-            for (int q = 0; q < 16; q += 4) {
-              const int col = n0 + wn * H * 32 + n * 32 + 8 * (q >> 2) + 4 * (l >> 5);
-              if (col < a.Nout) {
-                float h[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) h[u] = silu_f32(acc[m][n][q + u]) * acc[m][n + H][q + u];
-                *reinterpret_cast<u32x2_t*>(orow + col) =
-                    u32x2_t{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
-              }
-            }
-          }
-        } else {
-          const float gw = a.topk_w ? a.topk_w[a.sorted_slot[p]] : 1.0f;
-#pragma unroll
-          for (int n = 0; n < NB; ++n) {
-#pragma unroll
-            for (int q = 0; q < 16; q += 4) {
-              const int col = n0 + wn * NB * 32 + n * 32 + 8 * (q >> 2) + 4 * (l >> 5);
-              if (col < a.Nout)
-                *reinterpret_cast<u32x2_t*>(orow + col) =
-                    u32x2_t{pack_bf16x2(acc[m][n][q] * gw, acc[m][n][q + 1] * gw),
-                            pack_bf16x2(acc[m][n][q + 2] * gw, acc[m][n][q + 3] * gw)};
-            }
+            for (int q = 0; q < 16; ++q)
+              h[q] = kGateUp ? silu_f32(acc[m][n][q]) * acc[m][n + (kGateUp ? H : 0)][q]
+                             : acc[m][n][q] * gw[kGateUp ? 0 : m];
+            *reinterpret_cast<u32x4_t*>(orow + col) =
+                u32x4_t{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]),
+                        pack_bf16x2(h[4], h[5]), pack_bf16x2(h[6], h[7])};
+            *reinterpret_cast<u32x4_t*>(orow + col + 8) =
+                u32x4_t{pack_bf16x2(h[8], h[9]), pack_bf16x2(h[10], h[11]),
+                        pack_bf16x2(h[12], h[13]), pack_bf16x2(h[14], h[15])};
           }
         }
       }
     }
+
+    if (!has_next) break;
+    item = item_n;
+    base += nK;
+    cj = xj, c0 = x0, ce = xe, n0c = n0x;
+    xj = yj, x0 = y0, xe = ye, n0x = n0y;
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) rows_cur[i] = rows_nxt[i];
+    parity ^= 1;
   }
+#undef MOE_ISSUE_STAGE
 }
 
 // ---- float32 path: plain VALU dot products over the same tile schedule
@@ -469,9 +582,9 @@ __global__ __launch_bounds__(256) void grouped_f32_kernel(GemmArgs a) {
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int g = item / a.n_tiles_n;
     const int nt = item % a.n_tiles_n;
-    const int2 tile = a.tiles[g];
+    const int4 tile = a.tiles[g];
     const int j = tile.x, row0 = tile.y;
-    const int row_end = a.offsets[j + 1];
+    const int row_end = tile.z;
     for (int o = threadIdx.x; o < kF32BM * kF32BN; o += blockDim.x) {
       const int r = o / kF32BN, c = o % kF32BN;
       const int p = row0 + r;
@@ -501,6 +614,15 @@ __global__ __launch_bounds__(256) void grouped_f32_kernel(GemmArgs a) {
 // ---- launch plumbing
 int g_num_cu = 0;
 
+// MOE_MI355X_MAX_WORKGROUPS caps the persistent GEMM grid (rounded up to a
+// multiple of 8).  Results do not depend on it: every output element comes
+// from one tile with a fixed K order.  Tests use it to give each workgroup
+// many items.
+long long max_workgroups() {
+  const char* v = getenv("MOE_MI355X_MAX_WORKGROUPS");
+  return v ? atoll(v) : 0;
+}
+
 int num_cu() {
   if (g_num_cu == 0) {
     int dev = 0, n = 0;
@@ -528,9 +650,12 @@ hipError_t launch_gemm(const GemmArgs& a, long long max_items, hipStream_t st) {
   long long grid = (long long)num_cu() * kMinBlocks;
   const long long need = (max_items + kNumXcd - 1) / kNumXcd * kNumXcd;
   if (need < grid) grid = need;
+  if (const long long cap = max_workgroups(); cap > 0 && cap < grid) grid = cap;
   grid = (grid + kNumXcd - 1) / kNumXcd * kNumXcd;
   if (grid < kNumXcd) grid = kNumXcd;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::kThreads), C::kLds, st, a);
+  // stages, then the FP8 scales of two items
+  const size_t lds = (size_t)kStages * C::kStage + (kFP8 ? 2u * C::kScaleSets * (a.K / 128) * 4 : 0);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::kThreads), lds, st, a);
   return hipGetLastError();
 }
 
@@ -568,15 +693,15 @@ size_t max_tiles(const Shape& s, int bm) { return (size_t)((s.S + bm - 1) / bm) 
 FfnSchedule ffn_schedule_view(const Shape& s, void* ws) {
   unsigned char* p = static_cast<unsigned char*>(ws);
   FfnSchedule v;
-  v.tiles = reinterpret_cast<int2*>(p);
-  v.ntiles = reinterpret_cast<int*>(p + align_up(max_tiles(s, 32) * sizeof(int2)));
+  v.tiles = reinterpret_cast<int4*>(p);
+  v.ntiles = reinterpret_cast<int*>(p + align_up(max_tiles(s, 32) * sizeof(int4)));
   v.bm = tile_bm(s);
   return v;
 }
 
 size_t ffn_ws_bytes(const Shape& s) {
   // schedule (at the smallest tile) + tile count + h [S][F]
-  return align_up(max_tiles(s, 32) * sizeof(int2)) + align_up(sizeof(int)) +
+  return align_up(max_tiles(s, 32) * sizeof(int4)) + align_up(sizeof(int)) +
          align_up((size_t)s.S * s.F * act_bytes(s));
 }
 
@@ -587,10 +712,10 @@ hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
                       hipStream_t st, bool schedule_ready, hipEvent_t const* ev) {
   if (s.S == 0) return hipSuccess;
   const FfnSchedule sv = ffn_schedule_view(s, ws);
-  int2* tiles = sv.tiles;
+  int4* tiles = sv.tiles;
   int* ntiles = sv.ntiles;
   uint16_t* h = reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(ws) +
-                                            align_up(max_tiles(s, 32) * sizeof(int2)) +
+                                            align_up(max_tiles(s, 32) * sizeof(int4)) +
                                             align_up(sizeof(int)));
   const int bm = sv.bm;
   hipError_t e = hipSuccess;

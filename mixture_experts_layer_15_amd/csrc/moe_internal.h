@@ -37,7 +37,7 @@ hipError_t route(const Shape& s, const void* x, const void* w_router, const floa
 
 // ---- ffn.hip (tile schedule shared with the permutation)
 struct FfnSchedule {
-  int2* tiles;   // (local expert, first row) of every M tile
+  int4* tiles;   // (local expert, first row, expert's end row, 0) of every M tile
   int* ntiles;   // number of M tiles
   int bm;        // M tile height
 };

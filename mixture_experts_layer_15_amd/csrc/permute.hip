@@ -134,7 +134,7 @@ constexpr long long kSmallSlots = 8192;
 
 __global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(
     const int32_t* __restrict__ idx, int S, int e0, int El, int nbits, int32_t* counts,
-    int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos, int bm, int2* tiles, int* ntiles) {
+    int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos, int bm, int4* tiles, int* ntiles) {
   __shared__ int hist[kMaxExperts];
   __shared__ int base[kMaxExperts];
   __shared__ int scan[kSmallThreads];
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(
     offsets[tid] = off;
     base[tid] = off;
     if (tiles)
-      for (int i = 0; i < nt; ++i) tiles[tfirst + i] = make_int2(tid, off + i * bm);
+      for (int i = 0; i < nt; ++i) tiles[tfirst + i] = make_int4(tid, off + i * bm, off + cnt, 0);
   }
   if (tid == El - 1) {
     offsets[El] = incl & 0xffff;

@@ -156,6 +156,39 @@ def test_small_full_parity(case):
     check(pr, forward(pr))
 
 
+# Cases whose GEMMs run every tile plan with long K loops (at least 8 K stages,
+# so the next item's stages are loaded inside the running item's K loop).
+# Capping the persistent grid at 8 workgroups gives each workgroup many items.
+MULTI = {
+    "decode_plan": synth.WORKLOADS["decode"].replace(
+        name="bf16_T96_d512_E16_k4_F512", T=96, d=512, E=16, num_local=16, k=4, F=512, seed=61),
+    "wide_plan": synth.WORKLOADS["prefill"].replace(
+        name="bf16_T900_d512_E8_k2_F384_zipf", T=900, d=512, E=8, num_local=8, k=2, F=384,
+        seed=62),
+    "big_plan": synth.WORKLOADS["mixtral"].replace(
+        name="bf16_T2300_d512_E4_k2_F512_gauss", T=2300, d=512, E=4, num_local=4, k=2, F=512,
+        seed=63),
+    "fp8_plan": synth.WORKLOADS["dsv3_rank"].replace(
+        name="fp8_T1500_d512_E16_local4-11_k4_F512", T=1500, d=512, E=16, num_local=8,
+        expert_begin=4, k=4, F=512, seed=64),
+    "fp8_decode_plan": synth.WORKLOADS["dsv3_rank"].replace(
+        name="fp8_T64_d512_E32_local0-15_k4_F512", T=64, d=512, E=32, num_local=16,
+        expert_begin=0, k=4, F=512, seed=65),
+}
+
+
+@pytest.mark.parametrize("case", list(MULTI))
+def test_many_items_per_workgroup(case, monkeypatch):
+    pr = synth.make_problem(MULTI[case])
+    g = upload(pr)
+    wide = forward(pr, g)
+    monkeypatch.setenv("MOE_MI355X_MAX_WORKGROUPS", "8")
+    narrow = forward(pr, g)
+    # the same tiles computed in another order: identical bits
+    assert torch.equal(narrow["out"], wide["out"])
+    check(pr, narrow)
+
+
 @pytest.mark.parametrize("case", ["T1", "k_equals_E", "E1_k1", "E512_k8"])
 def test_edge_shapes(case):
     base = synth.WORKLOADS["decode"]
