@@ -63,7 +63,9 @@
  * C++ exception crosses this interface.
  *
  * Limits: 1 <= k <= E <= 512; T*k < 2^31; d, F multiples of 128 and
- * at most 65536; T = 0 is accepted and enqueues nothing (no output is written).
+ * at most 65536; x (T*d elements) and one expert's weight matrix (F*d
+ * elements) under 4 GiB each; T = 0 is accepted and enqueues nothing (no
+ * output is written).
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H

@@ -60,6 +60,7 @@ __global__ __launch_bounds__(kMaxExperts) void ffn_schedule_kernel(const int32_t
 
 struct GemmArgs {
   const uint16_t* A;           // gate/up: x [T][K]; down: h [S][K]  (bf16)
+  uint32_t a_bytes;            // bytes of A (gate/up: x)
   const int32_t* sorted_slot;  // gate/up gather
   int k;                       // top-k (slot -> token)
   const void* W0;              // gate (gate/up) or down weights
@@ -141,6 +142,29 @@ __device__ __forceinline__ void lds_dma16(const void* src, unsigned char* lds) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 #else
   (void)src;
+  (void)lds;
+#endif
+}
+
+// Raw buffer resource over `bytes` bytes at `base` (wave-uniform): loads
+// through it take a 32-bit per-lane offset, and offsets at or past `bytes`
+// read zeros instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// One 16-byte buffer -> LDS load per lane (buffer_load_dwordx4 ... lds): lane
+// i's 16 bytes, from voffset + soffset in the buffer, land at lds + 16 i.
+__device__ __forceinline__ void lds_dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voffset,
+                                              uint32_t soffset, unsigned char* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voffset, soffset, 0, 0);
+#else
+  (void)r;
+  (void)voffset;
+  (void)soffset;
   (void)lds;
 #endif
 }
@@ -276,47 +300,60 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
     }
   };
 
-  // this lane's source chunk of every LDS-DMA load of an item's stage 0
-  const unsigned char* srcA[C::kLoadsA];
-  const unsigned char* srcB[C::kLoadsB];
+  // Sources of an item's LDS-DMA loads: buffer resources (scalar registers)
+  // and one 32-bit offset per lane and load (stage 0); a stage's K offset is
+  // a scalar added at issue.  (The host limits x, and one expert's weight
+  // matrix, to 4 GiB.)
+  __amdgpu_buffer_rsrc_t rsA, rsB0, rsB1;  // A rows; gate or down weights; up weights
+  uint32_t offA[C::kLoadsA];
+  uint32_t offB[C::kLoadsB];
+  // weight instruction i of this wave reads up rows (one half of the tile)
+  auto b_up = [&](int i) -> bool {
+    return kGateUp && ((wave * C::kLoadsB + i) * kWave) / C::kChunksB >= BNW / 2;
+  };
   auto set_src = [&](int j, int row0, int row_end, int n0, const int* rows) {
+    j = __builtin_amdgcn_readfirstlane(j);
+    row0 = __builtin_amdgcn_readfirstlane(row0);
+    row_end = __builtin_amdgcn_readfirstlane(row_end);
+    const uint32_t arow_bytes = (uint32_t)a.K * 2;
+    rsA = kGateUp ? buffer_rsrc(a.A, a.a_bytes)
+                  : buffer_rsrc(reinterpret_cast<const unsigned char*>(a.A) +
+                                    (size_t)row0 * arow_bytes,
+                                (uint32_t)(row_end - row0) * arow_bytes);
 #pragma unroll
     for (int i = 0; i < C::kLoadsA; ++i) {
       const int P = (wave * C::kLoadsA + i) * kWave + l;  // 16-byte chunk position
       const int r = P / C::kChunksA;
       const int c = (P % C::kChunksA) ^ ((r / (256 / C::kRowA)) % C::kChunksA);
-      const long long arow = kGateUp ? (long long)(rows[kGateUp ? i : 0] / a.k)
-                                     : (long long)min(row0 + r, row_end - 1);
-      srcA[i] = reinterpret_cast<const unsigned char*>(a.A + arow * a.K) + c * 16;
+      const uint32_t arow = kGateUp ? (uint32_t)(rows[kGateUp ? i : 0] / a.k)
+                                    : (uint32_t)min(r, row_end - 1 - row0);
+      offA[i] = arow * arow_bytes + c * 16;
     }
+    const uint32_t wmat = (uint32_t)a.Nout * a.K * welem;  // bytes of one expert's matrix
+    rsB0 = buffer_rsrc(static_cast<const unsigned char*>(a.W0) + (size_t)j * wmat, wmat);
+    rsB1 = kGateUp ? buffer_rsrc(static_cast<const unsigned char*>(a.W1) + (size_t)j * wmat, wmat)
+                   : rsB0;
 #pragma unroll
     for (int i = 0; i < C::kLoadsB; ++i) {
       const int P = (wave * C::kLoadsB + i) * kWave + l;
       const int r = P / C::kChunksB;
       const int c = (P % C::kChunksB) ^ ((r / (256 / C::kRowB)) % C::kChunksB);
-      const unsigned char* base;
-      int wrow;
-      if (kGateUp) {
-        const bool up = r >= BNW / 2;
-        wrow = min(n0 + feat_of_row(up ? r - BNW / 2 : r), a.Nout - 1);
-        base = static_cast<const unsigned char*>(up ? a.W1 : a.W0);
-      } else {
-        wrow = min(n0 + feat_of_row(r), a.Nout - 1);
-        base = static_cast<const unsigned char*>(a.W0);
-      }
-      srcB[i] = base + ((long long)j * a.Nout + wrow) * a.K * welem + c * 16;
+      const int rr = (kGateUp && r >= BNW / 2) ? r - BNW / 2 : r;
+      const uint32_t wrow = (uint32_t)min(n0 + feat_of_row(rr), a.Nout - 1);
+      offB[i] = wrow * (uint32_t)(a.K * welem) + c * 16;
     }
   };
 
-  // stage Q of the item srcA/srcB point at, into the buffer of pipeline stage G
+  // stage Q of the item set_src chose, into the buffer of pipeline stage G
 #define MOE_ISSUE_STAGE(Q, G)                                                                   \
   do {                                                                                          \
     unsigned char* sb_ = smem + ((G) % kStages) * C::kStage;                                    \
     _Pragma("unroll") for (int i = 0; i < C::kLoadsA; ++i)                                      \
-        lds_dma16(srcA[i] + (long long)(Q) * kBK * 2, sb_ + (wave * C::kLoadsA + i) * 1024);    \
+        lds_dma16_buf(rsA, offA[i], (uint32_t)(Q) * kBK * 2,                                    \
+                      sb_ + (wave * C::kLoadsA + i) * 1024);                                    \
     _Pragma("unroll") for (int i = 0; i < C::kLoadsB; ++i)                                      \
-        lds_dma16(srcB[i] + (long long)(Q) * kBK * welem,                                       \
-                  sb_ + C::kStageA + (wave * C::kLoadsB + i) * 1024);                            \
+        lds_dma16_buf(b_up(i) ? rsB1 : rsB0, offB[i], (uint32_t)(Q) * kBK * welem,              \
+                      sb_ + C::kStageA + (wave * C::kLoadsB + i) * 1024);                       \
   } while (0)
 
   int item = it_begin + slot;
@@ -729,6 +766,7 @@ hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
 
   GemmArgs gu{};
   gu.A = static_cast<const uint16_t*>(x);
+  gu.a_bytes = (uint32_t)((size_t)s.T * s.d * act_bytes(s));
   gu.sorted_slot = sorted_slot;
   gu.k = s.k;
   gu.W0 = w_gate;
@@ -745,6 +783,7 @@ hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
 
   GemmArgs dn = gu;
   dn.A = h;
+  dn.a_bytes = 0;  // unused: the down GEMM reads h through per-tile resources
   dn.W0 = w_down;
   dn.W1 = nullptr;
   dn.S0 = s_down;

@@ -31,6 +31,12 @@ moe_status_t check_problem(const moe_problem_t* p, Shape* s) {
   if (p->E > moe::kMaxExperts || p->d > 65536 || p->F > 65536) return MOE_ERR_UNSUPPORTED;
   const long long S = (long long)p->T * p->k;
   if (S >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
+  // the expert GEMMs address x and one expert's weight matrix with 32-bit
+  // offsets
+  const long long ab = p->act == MOE_F32 ? 4 : 2;
+  const long long wb = p->weight == MOE_F32 ? 4 : p->weight == MOE_BF16 ? 2 : 1;
+  if ((long long)p->T * p->d * ab >= (1LL << 32) || (long long)p->F * p->d * wb >= (1LL << 32))
+    return MOE_ERR_UNSUPPORTED;
   s->T = p->T;
   s->d = p->d;
   s->E = p->E;
