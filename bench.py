@@ -42,10 +42,26 @@ PEAK_FP32_TFLOPS = 157.3       # fp32 vector / matrix
 ACT_BYTES = {"f32": 4, "bf16": 2}
 W_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
 
-# Dominant-kernel names as they appear in a rocprofv3 kernel trace.
-KERNEL_NAMES = {
-    "gate_up": "grouped_gemm_kernel<{mb}, {wm}, {nb}, {wn}, true, {fp8}, {mnb}>",
-}
+
+
+def gate_up_kernel_name(wl: synth.Workload) -> str:
+    """The gate/up kernel the library launches for this workload, as a
+    rocprofv3 kernel trace names it (the library's tile plan: decode tiles when
+    an expert averages at most 64 slots, then FP8, then 256x256 tiles from
+    1024 slots per expert, else 128x512)."""
+    S, El = wl.T * wl.k, wl.num_local
+    if wl.weight == "f32":
+        return "grouped_f32_kernel<true>"
+    fp8 = str(wl.weight == "fp8").lower()
+    if S <= 64 * El:
+        args = f"1, 1, 2, 4, true, {fp8}, 64, 4, {2 if wl.weight == 'fp8' else 1}"
+    elif wl.weight == "fp8":
+        args = "2, 2, 4, 2, true, true, 64, 4, 1"
+    elif S >= 1024 * El:
+        args = "2, 4, 4, 2, true, false, 32, 4, 1"
+    else:
+        args = "2, 2, 4, 4, true, false, 32, 4, 1"
+    return f"grouped_gemm_kernel<{args}>"
 
 
 def expert_bytes(d: int, F: int, wfmt: str, n_experts: int, with_scales: bool = True) -> int:
@@ -101,21 +117,22 @@ class HipEvents:
 def measured_traffic(workload: str, kernel: str):
     """HBM bytes per dispatch of the dominant kernel from the committed
     rocprofv3 FETCH_SIZE/WRITE_SIZE runs (scaled by the copy-kernel
-    calibration), or None when they were taken on other kernel sources or
-    another workload."""
+    calibration), or None when they were taken on other kernel sources or no
+    record covers this workload and kernel."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "gate_up_decode_pmc.json")
+    path = os.path.join(ROOT, "profiles", "gate_up_pmc.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
     m = hashlib.sha256()
     for f in rec["source_files"]:
         m.update(open(os.path.join(ROOT, f), "rb").read())
-    if m.hexdigest() != rec["source_sha256"] or rec["workload"] != workload:
+    if m.hexdigest() != rec["source_sha256"]:
         return None
-    if not rec["kernel"].startswith(kernel):
-        return None
-    return int(rec["traffic_bytes_per_dispatch"])
+    for r in rec["records"]:
+        if r["workload"] == workload and r["kernel"].startswith(kernel):
+            return int(r["traffic_bytes_per_dispatch"])
+    return None
 
 
 def cpu_baseline(pr: synth.Problem, logits: torch.Tensor, budget_s: float) -> dict:
@@ -247,10 +264,7 @@ def main() -> None:
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
         if wl.weight == "fp8":
             roof["frac_of_fp8_peak"] = round(achieved / PEAK_FP8_TFLOPS, 4)
-    bm, mb, wm = (32, 1, 1) if wl.T * wl.k <= 64 * wl.num_local else (128, 2, 2)
-    nb, wn = (2, 4) if bm == 32 else (4, 2)
-    roof["kernel"] = KERNEL_NAMES["gate_up"].format(
-        mb=mb, wm=wm, nb=nb, wn=wn, fp8=str(wl.weight == "fp8").lower(), mnb=2 if bm == 32 else 1)
+    roof["kernel"] = gate_up_kernel_name(wl)
     roof["traffic"] = measured_traffic(wl.name, roof["kernel"])
     roof["kernel_ms"] = round(stage_ms["gate_up"], 5)
     roof["bytes_per_launch"] = alg["gu_bytes"]
