@@ -47,7 +47,10 @@
  *    one byte each) with float32 scales per 128x128 block of the stored
  *    matrix.  Supported (act, weight) pairs: (F32, F32), (BF16, BF16),
  *    (BF16, FP8_E4M3).  Accumulation is float32; intermediate h is rounded
- *    to the activation format.
+ *    to the activation format.  FP8 block scales are finite, and each is 0
+ *    (the block contributes nothing) or between 2^-100 and 2^100 in
+ *    magnitude: the GEMMs fold them in by rescaling a float32 accumulator
+ *    from one 128-deep K block to the next.
  *  - Expert weights are stored "out x in" (the math matrices transposed):
  *      w_gate, w_up : [E_l][F][d]      w_down : [E_l][d][F]
  *      s_gate, s_up : [E_l][F/128][d/128]   s_down : [E_l][d/128][F/128]

@@ -13,18 +13,18 @@
 //   down:     y[p] = (h[p] Wd_j) * gate(p)
 //
 // Structure (bf16 activations; bf16 or FP8-E4M3 weights):
-//  * a one-workgroup schedule kernel splits every expert segment into M tiles
-//    of BM rows and writes the (expert, first row) list and its length;
+//  * the permutation (or a one-workgroup schedule kernel) splits every expert
+//    segment into M tiles of BM rows: (expert, first row, end row) per tile;
 //  * a persistent GEMM kernel walks items (M tile, N tile); the items are cut
 //    into eight contiguous ranges, one per XCD (workgroup b runs on XCD b % 8),
 //    so items that share an A tile or a weight tile meet in the same L2;
-//  * per item, a K loop of 64-deep steps: global -> registers (A rows gathered
-//    through sorted_slot, weight rows streamed; FP8 codes widened exactly to
-//    bf16) -> LDS (double buffered, 16-byte chunks XOR-swizzled by row) ->
-//    MFMA 32x32x16 bf16 with float32 accumulation;
-//  * FP8 weights carry a float32 scale per 128x128 block: the MFMA partial of
-//    each 128-deep K block is accumulated separately and added to the running
-//    sum times its block's scale, so the weights enter MFMA unrounded;
+//  * per item, a K loop over a ring of LDS stages filled by LDS-DMA (buffer
+//    loads straight into LDS; A rows gathered through sorted_slot, weight rows
+//    streamed; 16-byte chunks XOR-swizzled by row for the 64 LDS banks) ->
+//    MFMA 32x32x16 bf16 with float32 accumulation, weights as the A operand;
+//  * FP8 weights: raw codes through LDS, widened exactly to bf16 at use, and
+//    a float32 scale per 128x128 block folded in by rescaling the accumulator
+//    at each 128-deep K block, so the weights enter MFMA unrounded;
 //  * epilogues: silu(gate) * up rounded to bf16 (gate/up), or the product
 //    times the token's gate (down).
 #include <stdlib.h>
@@ -197,7 +197,7 @@ struct Cfg {
   static constexpr int kLoadsB = kStageB / (1024 * kWaves);
   static constexpr int kLoads = kLoadsA + kLoadsB;
   static constexpr int kSteps = kBK / 16;                     // MFMA K steps per stage
-  static constexpr int kScaleSets = kFP8 ? (kGateUp ? 2 : BNW / 128) : 0;
+  static constexpr int kScaleSets = kFP8 ? BNW / 128 : 0;  // 128-row weight blocks per tile
   static constexpr int kMaxKBlocks = 65536 / 128;
   static constexpr int kLds = kStages * kStage + 2 * kScaleSets * kMaxKBlocks * 4;
   static_assert(kBK == 32 || kBK == 64, "K step");
@@ -206,8 +206,8 @@ struct Cfg {
   static_assert(kStages >= 2 && (kStages - 1) * kLoads < 64, "vmcnt budget");
   static_assert(kLds <= 160 * 1024, "LDS budget");
   static_assert(128 % kBK == 0, "a scale block spans whole K steps");
-  static_assert(!kFP8 || !kGateUp || BNW / 2 == 128, "gate/up scales: one 128-row block");
-  static_assert(!kFP8 || BNW % 128 == 0, "down scales: whole 128-row blocks");
+  static_assert(!kFP8 || (kGateUp ? (BNW / 2) % 128 == 0 : BNW % 128 == 0),
+                "FP8 scales: whole 128-row weight blocks per tile (per half for gate/up)");
   static_assert(!kFP8 || kBK == 64, "FP8 raw codes are double-buffered per step pair");
   static_assert(kSteps % 2 == 0, "fragment buffers alternate by step");
 };
@@ -269,6 +269,11 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
     return wn * NB * 32 + n * 32 + (l & 31);
   };
   const int arow_base = wm * MB * 32 + (l & 31);
+  // FP8: scale set (128-row weight block of the tile) of weight block n
+  auto sblk = [&](int n) -> int {
+    if (kGateUp) return (n < H ? 0 : C::kScaleSets / 2) + (wn * H * 32 + (n % H) * 32) / 128;
+    return (wn * NB * 32 + n * 32) / 128;
+  };
 
   // rows: gate/up: sorted_slot of the A row of each of this lane's LDS-DMA
   // chunks; down: sorted_slot of this lane's epilogue rows (for the gates)
@@ -291,9 +296,12 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
     for (int c0 = wave * kWave; c0 < n_sc; c0 += C::kThreads) {
       const int o = c0 + l;
       if (o < n_sc) {
+        // set sb: the tile's sb-th 128-row weight block (gate/up: gate blocks,
+        // then up blocks)
         const int sb = o / KB, kb = o % KB;
-        const float* S = (kGateUp && sb == 1) ? a.S1 : a.S0;
-        const int nblk = min(kGateUp ? n0 / 128 : n0 / 128 + sb, a.Nout / 128 - 1);
+        constexpr int kHalf = kGateUp ? C::kScaleSets / 2 : C::kScaleSets;
+        const float* S = (kGateUp && sb >= kHalf) ? a.S1 : a.S0;
+        const int nblk = min(n0 / 128 + sb % kHalf, a.Nout / 128 - 1);
         lds_dma4(S + ((long long)j * (a.Nout / 128) + nblk) * KB + kb,
                  reinterpret_cast<unsigned char*>(sc_lds + buf * n_sc + c0));
       }
@@ -459,16 +467,23 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
     }
 
     f32x16_t acc[MB][NB];
-    f32x16_t part[kFP8 ? MB : 1][kFP8 ? NB : 1];
 #pragma unroll
     for (int m = 0; m < MB; ++m)
 #pragma unroll
       for (int n = 0; n < NB; ++n) acc[m][n] = f32x16_t{};
+    // FP8 block scales.  acc[.][n] holds the running sum divided by rsc[n],
+    // the scale of the latest K block with a nonzero scale.  Entering a block
+    // with scale s multiplies acc by rsc / s and makes s the reference, so the
+    // MFMAs add the block's unscaled products (exact bf16 widenings of the
+    // codes) straight into acc; the end multiplies by rsc.  A block whose
+    // scale is 0 contributes nothing: its codes are masked to 0 (behind a
+    // wave-uniform flag, so other blocks pay one scalar branch).
+    float rsc[kFP8 ? NB : 1];
+    bool zblk[kFP8 ? NB : 1];
+    bool anyz = false;
     if constexpr (kFP8) {
 #pragma unroll
-      for (int m = 0; m < MB; ++m)
-#pragma unroll
-        for (int n = 0; n < NB; ++n) part[m][n] = f32x16_t{};
+      for (int n = 0; n < NB; ++n) rsc[n] = 1.0f, zblk[n] = false;
     }
 
     auto mfma_step = [&](int s, int buf) {
@@ -476,7 +491,8 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
       for (int n = 0; n < NB; ++n) {
         bf16x8_t bfr;
         if constexpr (kFP8) {
-          const u32x4_t r = raw8[(s >> 1) & 1][n];
+          u32x4_t r = raw8[(s >> 1) & 1][n];
+          if (anyz && zblk[n]) r = u32x4_t{0u, 0u, 0u, 0u};
           const u32x2_t lo = e4m3x4_to_bf16x4(r[(s & 1) * 2]);
           const u32x2_t hi = e4m3x4_to_bf16x4(r[(s & 1) * 2 + 1]);
           bfr = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
@@ -486,10 +502,7 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
 #pragma unroll
         for (int m = 0; m < MB; ++m) {
           // weights as the MFMA A operand: the result block is [feature][token]
-          if constexpr (kFP8)
-            part[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr, af[buf][m], part[m][n], 0, 0, 0);
-          else
-            acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr, af[buf][m], acc[m][n], 0, 0, 0);
+          acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr, af[buf][m], acc[m][n], 0, 0, 0);
         }
       }
     };
@@ -500,6 +513,28 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
     // stage ks + kStages and read stage ks + 1's first fragments while the
     // last step's MFMAs run.
     for (int ks = 0; ks < nK; ++ks) {
+      if constexpr (kFP8) {
+        if ((ks * kBK) % 128 == 0) {  // entering a 128-deep scale block
+          const int kb = (ks * kBK) / 128;
+          anyz = false;
+#pragma unroll
+          for (int n = 0; n < NB; ++n) {
+            const int bits = __builtin_amdgcn_readfirstlane(
+                __float_as_int(sc_lds[parity * n_sc + sblk(n) * KB + kb]));
+            zblk[n] = (bits & 0x7fffffff) == 0;
+            anyz = anyz || zblk[n];
+            if (!zblk[n]) {
+              const float sv = __int_as_float(bits);
+              if (kb > 0) {
+                const float ratio = rsc[n] / sv;
+#pragma unroll
+                for (int m = 0; m < MB; ++m) acc[m][n] *= ratio;
+              }
+              rsc[n] = sv;
+            }
+          }
+        }
+      }
 #pragma unroll
       for (int s = 0; s < C::kSteps; ++s) {
         if (s + 1 < C::kSteps) {
@@ -529,24 +564,12 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
           if (more) sched_alternate<MB + NB, MB * NB>();
         }
       }
-      if constexpr (kFP8) {
-        if ((ks + 1) % (128 / kBK) == 0) {  // end of a 128-deep scale block
-          const int kb = (ks * kBK) / 128;
-          float sc[NB];
+    }
+    if constexpr (kFP8) {
 #pragma unroll
-          for (int n = 0; n < NB; ++n) {
-            const int sb = kGateUp ? (n < H ? 0 : 1) : (wn * NB * 32 + n * 32) / 128;
-            sc[n] = sc_lds[parity * n_sc + sb * KB + kb];
-          }
+      for (int m = 0; m < MB; ++m)
 #pragma unroll
-          for (int m = 0; m < MB; ++m)
-#pragma unroll
-            for (int n = 0; n < NB; ++n) {
-              acc[m][n] += part[m][n] * sc[n];
-              part[m][n] = f32x16_t{};
-            }
-        }
-      }
+        for (int n = 0; n < NB; ++n) acc[m][n] *= rsc[n];
     }
 
     if (has_next) {
@@ -700,9 +723,9 @@ hipError_t launch_gemm(const GemmArgs& a, long long max_items, hipStream_t st) {
 // waves side by side along N, 64-deep K steps, 4 stages.  bf16 prefill: eight
 // waves of 64 x 128, 32-deep K steps and 4 stages, as 128 x 512 tiles when
 // experts hold a few hundred rows (less M padding) or 256 x 256 when they hold
-// a thousand or more (fewer bytes staged per MFMA).  FP8 weights: four waves
-// (each keeps a second accumulator set for the per-block scales), 128 x 256
-// tiles, 64-deep K steps and 4 stages.
+// a thousand or more (fewer bytes staged per MFMA).  FP8 weights: eight waves
+// of 64 x 128 in 128 x 512 tiles, 64-deep K steps (one byte per code) and 3
+// stages.
 enum class Plan { kF32, kDecode, kWide, kBig, kFp8 };
 
 Plan plan_of(const Shape& s) {
@@ -827,11 +850,11 @@ hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
       }
       break;
     case Plan::kFp8:
-      gu.n_tiles_n = ntn(s.F, 128);
-      dn.n_tiles_n = ntn(s.d, 256);
-      e = launch_gemm<2, 2, 4, 2, true, true, 64, 4, 1>(gu, mt * gu.n_tiles_n, st);
+      gu.n_tiles_n = ntn(s.F, 256);
+      dn.n_tiles_n = ntn(s.d, 512);
+      e = launch_gemm<2, 2, 4, 4, true, true, 64, 3, 1>(gu, mt * gu.n_tiles_n, st);
       if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-      if (e == hipSuccess) e = launch_gemm<2, 2, 4, 2, false, true, 64, 4, 1>(dn, mt * dn.n_tiles_n, st);
+      if (e == hipSuccess) e = launch_gemm<2, 2, 4, 4, false, true, 64, 3, 1>(dn, mt * dn.n_tiles_n, st);
       break;
     case Plan::kWide:
       gu.n_tiles_n = ntn(s.F, 256);

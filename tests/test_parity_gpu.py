@@ -189,6 +189,21 @@ def test_many_items_per_workgroup(case, monkeypatch):
     check(pr, narrow)
 
 
+@pytest.mark.parametrize("case", ["fp8_plan", "fp8_decode_plan"])
+def test_fp8_zero_and_spread_block_scales(case):
+    """Block scales that vary by up to 2^16 along K and blocks whose scale is 0
+    (their nonzero codes must contribute nothing): the kernels fold the scales
+    by rescaling the accumulator from block to block."""
+    pr = synth.make_problem(MULTI[case].replace(name=case + "_scales", seed=66))
+    g = torch.Generator().manual_seed(67)
+    for n in ("s_gate", "s_up", "s_down"):
+        s = getattr(pr, n)
+        f = torch.exp2(torch.randint(-8, 9, s.shape, generator=g).float())
+        f[torch.rand(s.shape, generator=g) < 0.15] = 0.0
+        setattr(pr, n, (s * f).contiguous())
+    check(pr, forward(pr))
+
+
 @pytest.mark.parametrize("case", ["T1", "k_equals_E", "E1_k1", "E512_k8"])
 def test_edge_shapes(case):
     base = synth.WORKLOADS["decode"]
