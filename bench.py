@@ -56,7 +56,7 @@ def gate_up_kernel_name(wl: synth.Workload) -> str:
     if S <= 64 * El:
         args = f"1, 1, 2, 4, true, {fp8}, 64, 4, {2 if wl.weight == 'fp8' else 1}"
     elif wl.weight == "fp8":
-        args = "2, 2, 4, 2, true, true, 64, 4, 1"
+        args = "2, 2, 4, 4, true, true, 64, 3, 1"
     elif S >= 1024 * El:
         args = "2, 4, 4, 2, true, false, 32, 4, 1"
     else:

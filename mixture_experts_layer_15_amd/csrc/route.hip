@@ -21,6 +21,8 @@
 //    on exactly those values; gates are exp(L_i - L_0) normalised over the k.
 // Every sum has a fixed order, so the logits (and hence the routing) are
 // bit-reproducible from run to run.
+#include <type_traits>
+
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -171,8 +173,59 @@ __global__ __launch_bounds__(kThreads) void router_partial_f32(PartialArgs a) {
   }
 }
 
+// Wave-wide maximum of a 64-bit key, on VALU lane exchanges only (DPP inside
+// rows of 16 lanes, then the gfx950 row-pair and half-wave swaps): every lane
+// ends with the maximum.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t key) {
+  auto dpp_step = [&](auto ctrl_tag) {
+    constexpr int kCtrl = decltype(ctrl_tag)::value;
+    const uint32_t lo = (uint32_t)key, hi = (uint32_t)(key >> 32);
+    const uint32_t plo = __builtin_amdgcn_update_dpp(0u, lo, kCtrl, 0xF, 0xF, false);
+    const uint32_t phi = __builtin_amdgcn_update_dpp(0u, hi, kCtrl, 0xF, 0xF, false);
+    const uint64_t p = ((uint64_t)phi << 32) | plo;
+    key = p > key ? p : key;
+  };
+  dpp_step(std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]: lane ^ 1
+  dpp_step(std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]: lane ^ 2
+  dpp_step(std::integral_constant<int, 0x141>{});  // row_half_mirror: the other quad of 8
+  dpp_step(std::integral_constant<int, 0x140>{});  // row_mirror: the other half of 16
+  // The swaps exchange a register between row pairs (16) and wave halves
+  // (32); each lane then holds its own value and its partner's, in some
+  // order, in the two results, for the high and low words alike.
+  {
+    const uint32_t lo = (uint32_t)key, hi = (uint32_t)(key >> 32);
+    const auto l2 = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto h2 = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    const uint64_t a = ((uint64_t)h2[0] << 32) | l2[0], b = ((uint64_t)h2[1] << 32) | l2[1];
+    key = a > b ? a : b;
+  }
+  {
+    const uint32_t lo = (uint32_t)key, hi = (uint32_t)(key >> 32);
+    const auto l2 = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto h2 = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    const uint64_t a = ((uint64_t)h2[0] << 32) | l2[0], b = ((uint64_t)h2[1] << 32) | l2[1];
+    key = a > b ? a : b;
+  }
+  return key;
+}
+
+// Selection key of (logit v, expert e): larger key = larger v, then smaller
+// e.  The float bits are mapped to an order-preserving unsigned integer
+// (after -0 -> +0, so that the two zeros tie as equal values do).
+__device__ __forceinline__ uint64_t select_key(float v, int e) {
+  const uint32_t b = __float_as_uint(v + 0.0f);
+  const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)ord << 32) | (uint32_t)~e;
+}
+__device__ __forceinline__ float key_value(uint64_t key) {
+  const uint32_t ord = (uint32_t)(key >> 32);
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord);
+}
+
 // One wave per token: logits = sum of the split partials (in split order) +
-// bias; then top-k by (-L, e) and the renormalised gates.
+// bias; then top-k by (-L, e) and the renormalised gates.  Lane l holds
+// experts l + 64 j (j < kPerLane).
+template <int kPerLane>
 __global__ __launch_bounds__(kThreads) void router_topk_kernel(const float* part, int nsplit,
                                                                const float* bias,
                                                                float* logits_out, int T, int E,
@@ -182,8 +235,7 @@ __global__ __launch_bounds__(kThreads) void router_topk_kernel(const float* part
   const int l = lane_id();
   const int t = blockIdx.x * (kThreads / kWave) + w;
   if (t >= T) return;
-  constexpr int kPerLane = kMaxExperts / kWave;  // 8
-  constexpr int kBatch = 8;                        // split partials loaded together
+  constexpr int kBatch = 8;  // split partials loaded together
   float v[kPerLane];
 #pragma unroll
   for (int j = 0; j < kPerLane; ++j) v[j] = 0.f;
@@ -205,53 +257,44 @@ __global__ __launch_bounds__(kThreads) void router_topk_kernel(const float* part
       }
     }
   }
+  uint64_t key[kPerLane];
 #pragma unroll
   for (int j = 0; j < kPerLane; ++j) {
     const int e = l + kWave * j;
-    float s = -INFINITY;
+    key[j] = 0;  // below every real key: never chosen
     if (e < E) {
-      s = v[j];
+      float s = v[j];
       if (bias) s += bias[e];
       if (logits_out) logits_out[(size_t)t * E + e] = s;
       if (s != s) s = -INFINITY;  // NaN never wins (inputs are expected finite)
+      key[j] = select_key(s, e);
     }
-    v[j] = s;
   }
-  uint32_t taken = 0;  // bit j: expert l + 64 j already chosen
   float first = 0.f;
-  float mine[kPerLane];  // chosen logit i is held by lane i % 64 in slot i / 64
+  float mine[kMaxExperts / kWave];  // chosen logit i is held by lane i % 64 in slot i / 64
 #pragma unroll
-  for (int q = 0; q < kPerLane; ++q) mine[q] = 0.f;
+  for (int q = 0; q < kMaxExperts / kWave; ++q) mine[q] = 0.f;
   for (int i = 0; i < k; ++i) {
-    float bv = -INFINITY;
-    int be = 0x7fffffff;
+    uint64_t best = 0;
 #pragma unroll
-    for (int j = 0; j < kPerLane; ++j) {
-      const int e = l + kWave * j;
-      if (e < E && !((taken >> j) & 1u) && (v[j] > bv || (v[j] == bv && e < be))) {
-        bv = v[j];
-        be = e;
-      }
-    }
+    for (int j = 0; j < kPerLane; ++j) best = key[j] > best ? key[j] : best;
+    best = wave_max_u64(best);
+    const int be = (int)~(uint32_t)best;
+    const float bv = key_value(best);
+    if ((be & (kWave - 1)) == l) {  // the owner retires the chosen expert
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, kWave);
-      const int oe = __shfl_xor(be, o, kWave);
-      if (ov > bv || (ov == bv && oe < be)) {
-        bv = ov;
-        be = oe;
-      }
+      for (int j = 0; j < kPerLane; ++j)
+        if (j == be / kWave) key[j] = 0;
     }
-    if ((be & (kWave - 1)) == l) taken |= 1u << (be / kWave);
     if (i == 0) first = bv;
 #pragma unroll
-    for (int q = 0; q < kPerLane; ++q)
+    for (int q = 0; q < kMaxExperts / kWave; ++q)
       if (i == q * kWave + l) mine[q] = bv;
     if (l == 0) topk_idx[(size_t)t * k + i] = be;
   }
   float psum = 0.f;
 #pragma unroll
-  for (int q = 0; q < kPerLane; ++q) {
+  for (int q = 0; q < kMaxExperts / kWave; ++q) {
     if (q * kWave + l < k) {
       mine[q] = expf(mine[q] - first);
       psum += mine[q];
@@ -259,7 +302,7 @@ __global__ __launch_bounds__(kThreads) void router_topk_kernel(const float* part
   }
   const float tot = wave_sum(psum);
 #pragma unroll
-  for (int q = 0; q < kPerLane; ++q)
+  for (int q = 0; q < kMaxExperts / kWave; ++q)
     if (q * kWave + l < k) topk_w[(size_t)t * k + q * kWave + l] = mine[q] / tot;
 }
 
@@ -300,8 +343,19 @@ hipError_t route(const Shape& s, const void* x, const void* w_router, const floa
     part = partials;
   }
   const int wpb = kThreads / kWave;
-  hipLaunchKernelGGL(router_topk_kernel, dim3((s.T + wpb - 1) / wpb), dim3(kThreads), 0, st, part,
-                     nsplit, b, logits, s.T, s.E, s.k, topk_idx, topk_w);
+  const dim3 tgrid((s.T + wpb - 1) / wpb);
+  if (s.E <= 64)
+    hipLaunchKernelGGL(router_topk_kernel<1>, tgrid, dim3(kThreads), 0, st, part, nsplit, b,
+                       logits, s.T, s.E, s.k, topk_idx, topk_w);
+  else if (s.E <= 128)
+    hipLaunchKernelGGL(router_topk_kernel<2>, tgrid, dim3(kThreads), 0, st, part, nsplit, b,
+                       logits, s.T, s.E, s.k, topk_idx, topk_w);
+  else if (s.E <= 256)
+    hipLaunchKernelGGL(router_topk_kernel<4>, tgrid, dim3(kThreads), 0, st, part, nsplit, b,
+                       logits, s.T, s.E, s.k, topk_idx, topk_w);
+  else
+    hipLaunchKernelGGL(router_topk_kernel<8>, tgrid, dim3(kThreads), 0, st, part, nsplit, b,
+                       logits, s.T, s.E, s.k, topk_idx, topk_w);
   return hipGetLastError();
 }
 
