@@ -91,7 +91,12 @@ typedef enum {
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype_t;
 
 /* Which call a workspace is sized for. */
-typedef enum { MOE_CALL_PERMUTE = 0, MOE_CALL_EXPERT_FFN = 1, MOE_CALL_FORWARD = 2 } moe_call_t;
+typedef enum {
+  MOE_CALL_PERMUTE = 0,
+  MOE_CALL_EXPERT_FFN = 1,
+  MOE_CALL_FORWARD = 2,
+  MOE_CALL_ROUTE = 3
+} moe_call_t;
 
 /* Problem shape.  T tokens, hidden size d, E global experts, top-k, SwiGLU
  * width F, local expert block [expert_begin, expert_begin + num_local);
@@ -118,14 +123,16 @@ const char* moe_status_string(moe_status_t s);
  *  router_bias [E] float32 or NULL (zero): added to the logits, so it moves
  *           both the selection and the gate values.
  *  logits   [T][E] float32, required: the output L (including the bias)
- *           when w_router != NULL (it also serves as the router's scratch),
- *           the input when w_router == NULL.
+ *           when w_router != NULL, the input when w_router == NULL.
  *  topk_idx [T][k] int32 output: global expert ids ordered by (-L, e).
  *  topk_w   [T][k] float32 output: renormalised gates (sum to 1 per token).
+ *  ws, ws_bytes: scratch of moe_workspace_size(p, MOE_CALL_ROUTE) bytes (the
+ *           router matrix transposed to [E][d] and K-split partial sums);
+ *           may be NULL / 0 when w_router == NULL.
  * The selection is taken on exactly the float32 values written to `logits`. */
 moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* w_router,
                        const float* router_bias, float* logits, int32_t* topk_idx,
-                       float* topk_w, void* stream);
+                       float* topk_w, void* ws, size_t ws_bytes, void* stream);
 
 /* Dispatch order ("Mechanics of Token Routing": tokens go to their expert):
  * a stable counting sort of the slots whose expert is local.

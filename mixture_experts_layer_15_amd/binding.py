@@ -18,7 +18,7 @@ LIB_PATH = os.environ.get("MOE_MI355X_LIB", os.path.join(PKG, "libmoe_mi355x.so"
 
 MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = range(3)
-MOE_CALL_PERMUTE, MOE_CALL_EXPERT_FFN, MOE_CALL_FORWARD = range(3)
+MOE_CALL_PERMUTE, MOE_CALL_EXPERT_FFN, MOE_CALL_FORWARD, MOE_CALL_ROUTE = range(4)
 MOE_FORWARD_EVENTS = 7
 
 FMT = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
@@ -60,7 +60,7 @@ def load_library() -> ctypes.CDLL:
     lib.moe_workspace_size.restype = sz
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
-    lib.moe_route.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+    lib.moe_route.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_permute.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_expert_ffn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_combine.argtypes = [P, vp, vp, vp, vp, vp]
@@ -108,9 +108,12 @@ def moe_workspace_size(p: Problem, call: int) -> int:
     return int(load_library().moe_workspace_size(ctypes.byref(p), call))
 
 
-def moe_route(p, x, w_router, router_bias, logits, topk_idx, topk_w, stream=None) -> None:
+def moe_route(p, x, w_router, router_bias, logits, topk_idx, topk_w, ws=None,
+              stream=None) -> None:
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     st = load_library().moe_route(ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(router_bias),
-                                  _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _stream(stream))
+                                  _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(ws), nbytes,
+                                  _stream(stream))
     _check("moe_route", st)
 
 

@@ -69,6 +69,8 @@ struct GemmArgs {
   const float* S1;             // FP8 scales for W1
   const float* topk_w;         // down epilogue gates, or null
   uint16_t* out;               // gate/up: h [S][Nout]; down: y [S][Nout]
+  float* out_f32;              // router: logits without bias [rows][Nout]
+  int rows;                    // router: token rows (one segment, tiles of BM)
   const int32_t* offsets;      // [El + 1]
   const int4* tiles;           // (expert, first row, expert's end row, 0)
   const int* ntiles;
@@ -212,10 +214,13 @@ struct Cfg {
   static_assert(kSteps % 2 == 0, "fragment buffers alternate by step");
 };
 
+// kRouter: the router products x W_r as one segment of `rows` token rows,
+// A = x read row by row, W0 = the router matrix stored [E][d], float32 output.
 template <int MB, int WM, int NB, int WN, bool kGateUp, bool kFP8, int kBK, int kStages,
-          int kMinBlocks>
+          int kMinBlocks, bool kRouter>
 __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel(GemmArgs a) {
   using C = Cfg<MB, WM, NB, WN, kGateUp, kFP8, kBK, kStages>;
+  static_assert(!kRouter || (!kGateUp && !kFP8), "router mode: plain bf16 GEMM");
   constexpr int BNW = C::BNW;
   constexpr int H = NB / 2;  // gate/up: column blocks per half
   extern __shared__ __align__(16) unsigned char smem[];
@@ -235,7 +240,12 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
   const int n_sc = C::kScaleSets * KB;  // scale floats per item
 
   // persistent, XCD-contiguous item ranges
-  const int n_mtiles = *a.ntiles;
+  const int n_mtiles = kRouter ? (a.rows + C::BM - 1) / C::BM : *a.ntiles;
+  // tile gt as (expert, first row, segment end row)
+  auto tile_at = [&](int gt, int opaque_zero) -> int4 {
+    if constexpr (kRouter) return make_int4(0, gt * C::BM, a.rows, 0);
+    return a.tiles[gt + opaque_zero];
+  };
   const int n_items = n_mtiles * a.n_tiles_n;
   const int xcd = blockIdx.x % kNumXcd;
   const int per_xcd = gridDim.x / kNumXcd;
@@ -284,9 +294,11 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
       if (kGateUp) {
         const int P = (wave * C::kLoadsA + i) * kWave + l;
         rows[i] = a.sorted_slot[min(row0 + P / C::kChunksA, row_end - 1)];
-      } else {
+      } else if (!kRouter) {
         const int p = row0 + arow_base + i * 32;
         rows[i] = p < row_end ? a.sorted_slot[p] : 0;
+      } else {
+        rows[i] = 0;
       }
     }
   };
@@ -372,12 +384,12 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
   int cj, c0, ce, n0c, xj = 0, x0 = 0, xe = 1, n0x = 0;
   {
     const int2 pl = place(item);
-    const int4 t = a.tiles[pl.x];
+    const int4 t = tile_at(pl.x, 0);
     cj = t.x, c0 = t.y, ce = t.z, n0c = pl.y;
   }
   if (item + per_xcd < it_end) {
     const int2 pl = place(item + per_xcd);
-    const int4 t = a.tiles[pl.x];
+    const int4 t = tile_at(pl.x, 0);
     xj = t.x, x0 = t.y, xe = t.z, n0x = pl.y;
   }
   int rows_cur[kRows];
@@ -444,7 +456,8 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
     if constexpr (!kGateUp) {
 #pragma unroll
       for (int m = 0; m < MB; ++m)
-        gw[m] = (a.topk_w && c0 + arow_base + m * 32 < ce) ? a.topk_w[rows_cur[m]] : 1.0f;
+        gw[m] = (!kRouter && a.topk_w && c0 + arow_base + m * 32 < ce) ? a.topk_w[rows_cur[m]]
+                                                                         : 1.0f;
     }
 
     // the next item's inputs and the tile of the item after it
@@ -459,7 +472,7 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
         // wait for it (and for every stage load in flight) right here
         int opaque_zero;
         asm volatile("v_mov_b32 %0, 0" : "=v"(opaque_zero));
-        const int4 t = a.tiles[place(item_n + per_xcd).x + opaque_zero];
+        const int4 t = tile_at(place(item_n + per_xcd).x, opaque_zero);
         yj = t.x, y0 = t.y, ye = t.z;
       }
       // the other scale buffer was last read by the previous item
@@ -591,6 +604,33 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
     // lane l holds token column l % 32 in its 16 registers); with the weight-row
     // permutation, register q is feature 16 (l / 32) + q of the block, so a
     // lane stores 16 consecutive features of one token row: two 16-byte stores.
+    if constexpr (kRouter) {
+      // float32 products; 16-byte stores where a run of 16 columns is whole
+      // and aligned, else one column at a time (no loads here: a load would
+      // wait for the next item's stages already in flight)
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        const int p = c0 + arow_base + m * 32;
+        if (p < ce) {
+          float* orow = a.out_f32 + (long long)p * a.Nout;
+#pragma unroll
+          for (int n = 0; n < NB; ++n) {
+            const int col = n0c + wn * NB * 32 + n * 32 + 16 * g;
+            if (col + 16 <= a.Nout && (a.Nout & 3) == 0) {
+#pragma unroll
+              for (int q = 0; q < 16; q += 4) {
+                *reinterpret_cast<f32x4_t*>(orow + col + q) =
+                    f32x4_t{acc[m][n][q], acc[m][n][q + 1], acc[m][n][q + 2], acc[m][n][q + 3]};
+              }
+            } else {
+#pragma unroll
+              for (int q = 0; q < 16; ++q)
+                if (col + q < a.Nout) orow[col + q] = acc[m][n][q];
+            }
+          }
+        }
+      }
+    } else {
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
       const int p = c0 + arow_base + m * 32;
@@ -614,6 +654,7 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
           }
         }
       }
+    }
     }
 
     if (!has_next) break;
@@ -696,10 +737,10 @@ int num_cu() {
 }
 
 template <int MB, int WM, int NB, int WN, bool kGateUp, bool kFP8, int kBK, int kStages,
-          int kMinBlocks>
+          int kMinBlocks, bool kRouter = false>
 hipError_t launch_gemm(const GemmArgs& a, long long max_items, hipStream_t st) {
   using C = Cfg<MB, WM, NB, WN, kGateUp, kFP8, kBK, kStages>;
-  auto kern = grouped_gemm_kernel<MB, WM, NB, WN, kGateUp, kFP8, kBK, kStages, kMinBlocks>;
+  auto kern = grouped_gemm_kernel<MB, WM, NB, WN, kGateUp, kFP8, kBK, kStages, kMinBlocks, kRouter>;
   static bool attr = false;
   if (!attr) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -749,6 +790,30 @@ int tile_bm(const Shape& s) {
 size_t max_tiles(const Shape& s, int bm) { return (size_t)((s.S + bm - 1) / bm) + s.El; }
 
 }  // namespace
+
+bool use_router_gemm(const Shape& s) { return s.act == kBF16 && s.T >= 1024; }
+
+hipError_t router_gemm(const Shape& s, const void* x, const void* w_router_t, float* prod,
+                       hipStream_t st) {
+  GemmArgs a{};
+  a.A = static_cast<const uint16_t*>(x);
+  a.a_bytes = (uint32_t)((size_t)s.T * s.d * 2);
+  a.k = 1;
+  a.W0 = w_router_t;
+  a.out_f32 = prod;
+  a.rows = s.T;
+  a.K = s.d;
+  a.Nout = s.E;
+  a.n_tiles_n = (s.E + 255) / 256;
+  a.group_m = 1;
+  // 32 x 256 tiles (four waves side by side along the experts); 64-row tiles
+  // once there are enough of them, which halves the router matrix re-reads
+  if (s.T >= 16384)
+    return launch_gemm<2, 1, 2, 4, false, false, 64, 4, 1, true>(
+        a, (long long)((s.T + 63) / 64) * a.n_tiles_n, st);
+  return launch_gemm<1, 1, 2, 4, false, false, 64, 4, 1, true>(
+      a, (long long)((s.T + 31) / 32) * a.n_tiles_n, st);
+}
 
 FfnSchedule ffn_schedule_view(const Shape& s, void* ws) {
   unsigned char* p = static_cast<unsigned char*>(ws);

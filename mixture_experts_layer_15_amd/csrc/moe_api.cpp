@@ -94,6 +94,8 @@ size_t moe_workspace_size(const moe_problem_t* p, int32_t call) {
       return moe::ffn_ws_bytes(s);
     case MOE_CALL_FORWARD:
       return forward_layout(s).total;
+    case MOE_CALL_ROUTE:
+      return moe::route_ws_bytes(s);
     default:
       return 0;
   }
@@ -117,18 +119,22 @@ const char* moe_status_string(moe_status_t s) {
 
 moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* w_router,
                        const float* router_bias, float* logits, int32_t* topk_idx,
-                       float* topk_w, void* stream) {
+                       float* topk_w, void* ws, size_t ws_bytes, void* stream) {
   Shape s;
   moe_status_t st = check_problem(p, &s);
   if (st != MOE_OK) return st;
   if (topk_idx == nullptr || topk_w == nullptr) return MOE_ERR_INVALID_ARGUMENT;
   if (w_router != nullptr && x == nullptr) return MOE_ERR_INVALID_ARGUMENT;
   if (logits == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+  if (w_router != nullptr) {
+    const size_t need = moe::route_ws_bytes(s);
+    if (need > 0 && ws == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+    if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  }
   if (s.T == 0) return MOE_OK;
-  // without scratch, the router's partial products go straight to `logits`
   const float* lin = w_router == nullptr ? logits : nullptr;
-  return from_hip(moe::route(s, x, w_router, router_bias, lin, logits, topk_idx, topk_w, logits,
-                             1, static_cast<hipStream_t>(stream)));
+  return from_hip(moe::route(s, x, w_router, router_bias, lin, logits, topk_idx, topk_w, ws,
+                             static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_permute(const moe_problem_t* p, const int32_t* topk_idx, int32_t* counts,
@@ -213,8 +219,8 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_forward_args_t* a, vo
   auto mark = [&](int i) { return a->events ? hipEventRecord(ev[i], strm) : hipSuccess; };
   hipError_t e = mark(0);
   if (e == hipSuccess)
-    e = moe::route(s, a->x, a->w_router, a->router_bias, lin, lout, idx, gw,
-                   reinterpret_cast<float*>(base + L.router), moe::router_splits(s), strm);
+    e = moe::route(s, a->x, a->w_router, a->router_bias, lin, lout, idx, gw, base + L.router,
+                   strm);
   if (e == hipSuccess) e = mark(1);
   const moe::FfnSchedule sched = moe::ffn_schedule_view(s, base + L.ffn);
   bool sched_ready = false;

@@ -27,13 +27,17 @@ inline int act_bytes(const Shape& s) { return s.act == kF32 ? 4 : 2; }
 // K splits of the router GEMM used by moe_forward, and the scratch they need.
 int router_splits(const Shape& s);
 size_t route_ws_bytes(const Shape& s);
-// w_router != null: partial products go to `partials` ([nsplit][T][E]; may be
-// `logits` itself when nsplit == 1), then logits = sum + bias are published to
-// `logits` (if non-null) and selected on.  w_router == null: `logits_in` holds
-// the final logits.
+// w_router != null: logits = x W_r + bias are published to `logits` and
+// selected on; scratch holds route_ws_bytes (the transposed router matrix and
+// K-split partials).  w_router == null: `logits_in` holds the final logits
+// (scratch may be null).
 hipError_t route(const Shape& s, const void* x, const void* w_router, const float* bias,
                  const float* logits_in, float* logits, int32_t* topk_idx, float* topk_w,
-                 float* partials, int nsplit, hipStream_t st);
+                 void* scratch, hipStream_t st);
+bool use_router_gemm(const Shape& s);
+// prod [T][E] = x W_r (float32 accumulation) from the router matrix stored [E][d]
+hipError_t router_gemm(const Shape& s, const void* x, const void* w_router_t, float* prod,
+                       hipStream_t st);
 
 // ---- ffn.hip (tile schedule shared with the permutation)
 struct FfnSchedule {

@@ -7,15 +7,19 @@
 // softmax over the k chosen logits (a softmax over all E renormalised over
 // the chosen k: the full denominator cancels).
 //
-// Two kernels:
-//  * router_partial: workgroup (row tile of 32 tokens, K split) computes the
-//    32 x E partial product over its K range on MFMA 32x32x16 (bf16) or with
-//    float32 FMAs (f32).  Inside a workgroup the four waves take interleaved
-//    32-deep K steps, each wave staging its own W_r rows through a private LDS
-//    buffer in W_r's natural [k][e] layout, with the next step's global loads
-//    in flight while the current step computes.  The four wave partials are
-//    added in a fixed order.  Splitting K across workgroups gives a decode
-//    batch (T = 64) enough workgroups to cover the chip.
+// Kernels:
+//  * router_partial (bf16): workgroup (32-token tile, K split) forms the
+//    32 x E partial products over its K range on MFMA 32x32x16; its four
+//    waves take interleaved K steps and their partials are added in a fixed
+//    order.  Splitting K gives a decode batch (T = 64) enough workgroups to
+//    cover the chip.  Two variants: "staged" reads W_r as stored ([d][E],
+//    coalesced along E) and transposes it through per-wave LDS buffers;
+//    "direct" (up to 32 experts, one 32-wide MFMA block) reads a transposed
+//    copy straight from global memory with a three-step prefetch.  float32:
+//    plain FMAs;
+//  * with many tokens and more than 128 experts, the expert GEMMs' pipeline
+//    in router mode on the transposed copy (one split);
+//  * router_transpose: W_r -> [E][d] in scratch, for the last two;
 //  * router_topk: one wave per token adds the K-split partials in a fixed
 //    order plus the bias, publishes the float32 logits, and selects the top k
 //    on exactly those values; gates are exp(L_i - L_0) normalised over the k.
@@ -30,19 +34,28 @@ namespace moe {
 namespace {
 
 constexpr int kBM = 32;        // tokens per partial workgroup
-constexpr int kCC = 128;       // expert columns per pass (4 MFMA blocks of 32)
-constexpr int kBK = 32;        // K rows of W_r per wave step
 constexpr int kThreads = 256;  // 4 waves
-constexpr int kStageStride = kCC + 8;  // bf16 per staged W_r row (padded)
-constexpr int kStageElems = kBK * kStageStride;
+constexpr int kWaves = kThreads / kWave;
 
 struct PartialArgs {
   const void* x;         // [T][d]
-  const void* w_router;  // [d][E]
+  const void* w;         // the router matrix: [d][E] (stored), or [E][d] (direct kernel)
   float* out;            // [nsplit][T][E] partial sums
   int T, d, E;
   int k_per_split;       // multiple of 128
 };
+
+// bf16 partial products, router matrix read in its stored [d][E] layout:
+// workgroup (32-token tile, K split), four waves taking interleaved 32-deep K
+// steps, each wave staging its own W_r rows (coalesced 16-byte loads along E)
+// through a private LDS buffer and reading them back transposed for the MFMA,
+// with the next step's loads in flight; 128 experts per pass; fixed-order sum
+// of the four wave partials.  Used for more than 32 experts.
+constexpr int kCC = 128;       // expert columns per pass (4 MFMA blocks of 32)
+constexpr int kBK = 32;        // K rows of W_r per wave step
+constexpr int kStageStride = kCC + 8;  // bf16 per staged W_r row (padded)
+constexpr int kStageElems = kBK * kStageStride;
+
 
 // Global loads of one 32-deep K step: W_r rows k0 + (l / 16) + 4 i, columns
 // c0 + 8 (l % 16) .. +8, and this lane's two A fragments.
@@ -73,7 +86,7 @@ struct PartialArgs {
 constexpr int kRouterLds = 4 * kBM * kCC * 4;  // 64 KB
 static_assert(4 * kStageElems * 2 <= kRouterLds, "stages fit the shared region");
 
-__global__ __launch_bounds__(kThreads) void router_partial_bf16(PartialArgs a) {
+__global__ __launch_bounds__(kThreads) void router_partial_staged(PartialArgs a) {
   __shared__ __align__(16) unsigned char smem[kRouterLds];
   uint16_t (*stage)[kStageElems] = reinterpret_cast<uint16_t (*)[kStageElems]>(smem);
   float (*red)[kBM][kCC] = reinterpret_cast<float (*)[kBM][kCC]>(smem);
@@ -85,7 +98,7 @@ __global__ __launch_bounds__(kThreads) void router_partial_bf16(PartialArgs a) {
   const int kbeg = split * a.k_per_split;
   const int nsteps = a.k_per_split / kBK;  // multiple of 4
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
-  const uint16_t* wr = static_cast<const uint16_t*>(a.w_router);
+  const uint16_t* wr = static_cast<const uint16_t*>(a.w);
   uint16_t* st = stage[w];
   float* out = a.out + (size_t)split * a.T * a.E;
 
@@ -154,10 +167,103 @@ __global__ __launch_bounds__(kThreads) void router_partial_bf16(PartialArgs a) {
 }
 #undef MOE_ROUTER_LOAD
 
+
+// bf16 partial products on MFMA 32x32x16, straight from global memory (the
+// router matrix transposed to [E][d] stays in L2; x rows stream once):
+// workgroup (32-token tile, K split), four waves taking interleaved 16-deep K
+// steps with loads three steps ahead, NB blocks of 32 experts per pass, and a
+// fixed-order sum of the four wave partials through LDS.  Used for up to 32
+// experts, where one 32-wide block covers them all.
+template <int NB>
+__global__ __launch_bounds__(kThreads) void router_partial_direct(PartialArgs a) {
+  __shared__ float red[kWaves][kBM][NB * 32];
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int l = lane_id();
+  const int t0 = blockIdx.x * kBM;
+  const int split = blockIdx.y;
+  const int kbeg = split * a.k_per_split;
+  const int nsteps = a.k_per_split / 16;
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  const uint16_t* wt = static_cast<const uint16_t*>(a.w);
+  float* out = a.out + (size_t)split * a.T * a.E;
+  // lane l: token row l % 32 of the tile (A) / expert l % 32 of a block (B),
+  // K values 8 (l / 32) .. + 8 of each 16-deep step
+  const uint16_t* xrow = x + (size_t)min(t0 + (l & 31), a.T - 1) * a.d + kbeg + 8 * (l >> 5);
+  for (int c0 = 0; c0 < a.E; c0 += NB * 32) {
+    const uint16_t* wrow[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      wrow[b] = wt + (size_t)min(c0 + b * 32 + (l & 31), a.E - 1) * a.d + kbeg + 8 * (l >> 5);
+    f32x16_t acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = f32x16_t{};
+    // this wave's steps are s = w, w + 4, ...; loads run three steps ahead of
+    // the MFMAs (four register sets).  Steps past the end contribute zero (A
+    // set to 0), so every wave runs whole groups of four steps.
+    bf16x8_t fa[4], fb[4][NB];
+    bool live[4];
+    auto load = [&](int s, int buf) {  // no branches: past the end, re-read the last step
+      const int sc = min(s, nsteps - 1);
+      live[buf] = s < nsteps;
+      fa[buf] = *reinterpret_cast<const bf16x8_t*>(xrow + 16 * sc);
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        fb[buf][b] = *reinterpret_cast<const bf16x8_t*>(wrow[b] + 16 * sc);
+    };
+    auto mfma = [&](int buf) {
+      // (the zero for a step past the end is chosen here, where the loads
+      // are waited for anyway)
+      const bf16x8_t av = live[buf] ? fa[buf] : bf16x8_t{};
+#pragma unroll
+      for (int b = 0; b < NB; ++b)  // tokens as the A operand: blocks are [token][expert]
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, fb[buf][b], acc[b], 0, 0, 0);
+    };
+    load(w, 0);
+    load(w + kWaves, 1);
+    load(w + 2 * kWaves, 2);
+    // (scheduling barriers keep the compiler from pulling loads down to their
+    // MFMAs, which would shorten the prefetch distance to nothing)
+    for (int s = w; s < nsteps; s += 4 * kWaves) {
+      load(s + 3 * kWaves, 3);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma(0);
+      __builtin_amdgcn_sched_barrier(0);
+      load(s + 4 * kWaves, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma(1);
+      __builtin_amdgcn_sched_barrier(0);
+      load(s + 5 * kWaves, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma(2);
+      __builtin_amdgcn_sched_barrier(0);
+      load(s + 6 * kWaves, 2);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma(3);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // wave partials -> LDS (lane l holds expert column l % 32 of each block,
+    // token rows 8 (q / 4) + 4 (l / 32) + q % 4), then the fixed-order sum
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        red[w][8 * (q >> 2) + 4 * (l >> 5) + (q & 3)][b * 32 + (l & 31)] = acc[b][q];
+    __syncthreads();
+    for (int o = tid; o < kBM * NB * 32; o += kThreads) {
+      const int r = o / (NB * 32), c = o % (NB * 32);
+      if (t0 + r < a.T && c0 + c < a.E)
+        out[(size_t)(t0 + r) * a.E + c0 + c] =
+            ((red[0][r][c] + red[1][r][c]) + red[2][r][c]) + red[3][r][c];
+    }
+    __syncthreads();
+  }
+}
+
 // float32 router: each thread forms whole dot products over its K range in order.
 __global__ __launch_bounds__(kThreads) void router_partial_f32(PartialArgs a) {
   const float* x = static_cast<const float*>(a.x);
-  const float* wr = static_cast<const float*>(a.w_router);
+  const float* wr = static_cast<const float*>(a.w);
   const int t0 = blockIdx.x * kBM;
   const int kbeg = blockIdx.y * a.k_per_split;
   float* out = a.out + (size_t)blockIdx.y * a.T * a.E;
@@ -306,6 +412,37 @@ __global__ __launch_bounds__(kThreads) void router_topk_kernel(const float* part
     if (q * kWave + l < k) topk_w[(size_t)t * k + q * kWave + l] = mine[q] / tot;
 }
 
+// W_r [d][E] -> [E][d] (bf16), 64 x 64 tiles through LDS with 16-byte global
+// accesses: the router kernels read each expert's weights as one contiguous
+// K row, like the expert GEMMs.
+__global__ __launch_bounds__(256) void router_transpose_bf16(const uint16_t* w, uint16_t* wt,
+                                                             int d, int E) {
+  __shared__ __align__(16) uint16_t tile[64][72];  // [k][e], 144-byte rows
+  const int k0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+  const bool full = (E % 8) == 0 && e0 + 64 <= E;
+  for (int i = threadIdx.x; i < 512; i += 256) {
+    const int r = i / 8, c = (i % 8) * 8;  // K row r, experts c .. c + 7
+    const uint16_t* src = w + (size_t)(k0 + r) * E + e0 + c;
+    if (full) {
+      *reinterpret_cast<u32x4_t*>(&tile[r][c]) = *reinterpret_cast<const u32x4_t*>(src);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) tile[r][c + j] = e0 + c + j < E ? src[j] : uint16_t(0);
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 512; i += 256) {
+    const int e = i / 8, c = (i % 8) * 8;  // expert e, K values c .. c + 7
+    if (e0 + e < E) {
+      u32x4_t v;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        v[j] = uint32_t(tile[c + 2 * j][e]) | (uint32_t(tile[c + 2 * j + 1][e]) << 16);
+      *reinterpret_cast<u32x4_t*>(wt + (size_t)(e0 + e) * d + k0 + c) = v;
+    }
+  }
+}
+
 }  // namespace
 
 int router_splits(const Shape& s) {
@@ -316,46 +453,86 @@ int router_splits(const Shape& s) {
   return splits;
 }
 
+namespace {
+// Router plans (bf16): up to 32 experts, the direct kernel on the transposed
+// matrix; many tokens and more than 128 experts, the GEMM pipeline on the
+// transposed matrix; otherwise the staged kernel on the stored matrix.
+bool gemm_router(const Shape& s) { return use_router_gemm(s) && s.E > 128; }
+bool direct_router(const Shape& s) { return s.act == kBF16 && s.E <= 32; }
+// scratch layout: the transposed router matrix [E][d] bf16 (direct and GEMM
+// plans), then the K-split partial sums [splits][T][E] float32 (more than one
+// split)
+size_t wt_bytes(const Shape& s) {
+  return (gemm_router(s) || direct_router(s)) ? align_up((size_t)s.E * s.d * 2) : 0;
+}
+int splits_of(const Shape& s) { return gemm_router(s) ? 1 : router_splits(s); }
+}  // namespace
+
 size_t route_ws_bytes(const Shape& s) {
-  return align_up((size_t)router_splits(s) * s.T * s.E * sizeof(float));
+  const int ns = splits_of(s);
+  return wt_bytes(s) + (ns > 1 ? align_up((size_t)ns * s.T * s.E * sizeof(float)) : 0);
 }
 
 hipError_t route(const Shape& s, const void* x, const void* w_router, const float* bias,
                  const float* logits_in, float* logits, int32_t* topk_idx, float* topk_w,
-                 float* partials, int nsplit, hipStream_t st) {
+                 void* scratch, hipStream_t st) {
   if (s.T == 0) return hipSuccess;
   const float* part;
   const float* b = bias;
+  int nsplit = 1;
+  float* publish = logits;
   if (w_router == nullptr) {
     part = logits_in;  // final logits given: no bias, nothing to publish
-    nsplit = 1;
     b = nullptr;
-    logits = nullptr;
+    publish = nullptr;
   } else {
-    PartialArgs pa{x, w_router, partials, s.T, s.d, s.E, s.d / nsplit};
+    unsigned char* ws = static_cast<unsigned char*>(scratch);
+    nsplit = splits_of(s);
+    float* partials = nsplit > 1 ? reinterpret_cast<float*>(ws + wt_bytes(s)) : logits;
+    hipError_t e = hipSuccess;
     const dim3 grid((s.T + kBM - 1) / kBM, nsplit);
-    if (s.act == kBF16)
-      hipLaunchKernelGGL(router_partial_bf16, grid, dim3(kThreads), 0, st, pa);
-    else
+    if (s.act == kBF16 && (gemm_router(s) || direct_router(s))) {
+      // the router matrix as [E][d]: every expert's weights one contiguous K row
+      uint16_t* wt = reinterpret_cast<uint16_t*>(ws);
+      hipLaunchKernelGGL(router_transpose_bf16, dim3(s.d / 64, (s.E + 63) / 64), dim3(256), 0,
+                         st, static_cast<const uint16_t*>(w_router), wt, s.d, s.E);
+      e = hipGetLastError();
+      if (e == hipSuccess && gemm_router(s)) {
+        // many tokens and experts: x W_r from the expert GEMMs' pipeline
+        e = router_gemm(s, x, wt, partials, st);
+      } else if (e == hipSuccess) {
+        PartialArgs pa{x, wt, partials, s.T, s.d, s.E, s.d / nsplit};
+        hipLaunchKernelGGL(router_partial_direct<1>, grid, dim3(kThreads), 0, st, pa);
+        e = hipGetLastError();
+      }
+    } else if (s.act == kBF16) {
+      PartialArgs pa{x, w_router, partials, s.T, s.d, s.E, s.d / nsplit};
+      hipLaunchKernelGGL(router_partial_staged, grid, dim3(kThreads), 0, st, pa);
+      e = hipGetLastError();
+    } else {
+      PartialArgs pa{x, w_router, partials, s.T, s.d, s.E, s.d / nsplit};
       hipLaunchKernelGGL(router_partial_f32, grid, dim3(kThreads), 0, st, pa);
-    hipError_t e = hipGetLastError();
+      e = hipGetLastError();
+    }
     if (e != hipSuccess) return e;
     part = partials;
   }
+  // (with one split the partials are `logits` itself: each lane reads its
+  // elements, then writes the final values back)
   const int wpb = kThreads / kWave;
   const dim3 tgrid((s.T + wpb - 1) / wpb);
   if (s.E <= 64)
     hipLaunchKernelGGL(router_topk_kernel<1>, tgrid, dim3(kThreads), 0, st, part, nsplit, b,
-                       logits, s.T, s.E, s.k, topk_idx, topk_w);
+                       publish, s.T, s.E, s.k, topk_idx, topk_w);
   else if (s.E <= 128)
     hipLaunchKernelGGL(router_topk_kernel<2>, tgrid, dim3(kThreads), 0, st, part, nsplit, b,
-                       logits, s.T, s.E, s.k, topk_idx, topk_w);
+                       publish, s.T, s.E, s.k, topk_idx, topk_w);
   else if (s.E <= 256)
     hipLaunchKernelGGL(router_topk_kernel<4>, tgrid, dim3(kThreads), 0, st, part, nsplit, b,
-                       logits, s.T, s.E, s.k, topk_idx, topk_w);
+                       publish, s.T, s.E, s.k, topk_idx, topk_w);
   else
     hipLaunchKernelGGL(router_topk_kernel<8>, tgrid, dim3(kThreads), 0, st, part, nsplit, b,
-                       logits, s.T, s.E, s.k, topk_idx, topk_w);
+                       publish, s.T, s.E, s.k, topk_idx, topk_w);
   return hipGetLastError();
 }
 

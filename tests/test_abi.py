@@ -63,7 +63,7 @@ FAKE = 0x1000  # never dereferenced: every call below fails its host checks
                                 dict(expert_begin=-1), dict(act=7), dict(E=0)])
 def test_invalid_shapes_rejected(lib, kw):
     p = _p(**kw)
-    st = lib.moe_route(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, FAKE, None)
+    st = lib.moe_route(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
     assert st == B.MOE_ERR_INVALID_ARGUMENT
     assert B.moe_workspace_size(p, B.MOE_CALL_FORWARD) == 0
 
@@ -85,9 +85,12 @@ def test_limits_are_unsupported_not_invalid(lib):
 
 def test_null_required_pointers(lib):
     p = _p()
-    assert lib.moe_route(ctypes.byref(p), FAKE, FAKE, None, None, None, FAKE, None) == 1
-    assert lib.moe_route(ctypes.byref(p), None, None, None, None, FAKE, FAKE, None) == 1
-    assert lib.moe_route(ctypes.byref(p), FAKE, FAKE, None, None, FAKE, FAKE, None) == 1
+    big = 1 << 30
+    assert lib.moe_route(ctypes.byref(p), FAKE, FAKE, None, None, None, FAKE, FAKE, big, None) == 1
+    assert lib.moe_route(ctypes.byref(p), None, None, None, None, FAKE, FAKE, FAKE, big, None) == 1
+    assert lib.moe_route(ctypes.byref(p), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, big, None) == 1
+    # a router matrix needs the scratch
+    assert lib.moe_route(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, big, None) == 1
     assert lib.moe_permute(ctypes.byref(p), None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == 1
     assert lib.moe_combine(ctypes.byref(p), FAKE, None, None, FAKE, None) == 1
     assert lib.moe_expert_ffn(ctypes.byref(p), FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None,
@@ -104,11 +107,14 @@ def test_null_required_pointers(lib):
 def test_workspace_too_small(lib):
     p = _p()
     for call, fn in ((B.MOE_CALL_PERMUTE, "perm"), (B.MOE_CALL_EXPERT_FFN, "ffn"),
-                     (B.MOE_CALL_FORWARD, "fwd")):
+                     (B.MOE_CALL_FORWARD, "fwd"), (B.MOE_CALL_ROUTE, "route")):
         need = B.moe_workspace_size(p, call)
         assert need > 0 and need % 256 == 0
         if fn == "perm":
             st = lib.moe_permute(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None)
+        elif fn == "route":
+            st = lib.moe_route(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, need - 1,
+                               None)
         elif fn == "ffn":
             st = lib.moe_expert_ffn(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
                                     None, None, FAKE, FAKE, need - 1, None)
@@ -122,7 +128,8 @@ def test_workspace_too_small(lib):
 def test_zero_tokens_enqueue_nothing(lib):
     p = _p(T=0)
     ws_need = B.moe_workspace_size(p, B.MOE_CALL_FORWARD)
-    assert lib.moe_route(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == 0
+    assert lib.moe_route(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                         None) == 0
     assert lib.moe_combine(ctypes.byref(p), FAKE, FAKE, None, FAKE, None) == 0
     a = B.ForwardArgs()
     a.x = a.w_router = a.w_gate = a.w_up = a.w_down = a.out = FAKE

@@ -144,6 +144,14 @@ SMALL = {
     "bf16_big_tiles": synth.WORKLOADS["mixtral"].replace(
         name="bf16_T2100_d384_E4_k2_F384_gauss", T=2100, d=384, E=4, num_local=4, k=2, F=384,
         seed=29),
+    # many tokens and more than 128 experts: router logits from the GEMM
+    # pipeline (E not a multiple of 16, then not of 4: masked logit columns)
+    "bf16_router_gemm": synth.WORKLOADS["prefill"].replace(
+        name="bf16_T1100_d384_E200_k6_F128_zipf", T=1100, d=384, E=200, num_local=200, k=6,
+        F=128, seed=30),
+    "bf16_router_gemm_odd_E": synth.WORKLOADS["prefill"].replace(
+        name="bf16_T1030_d256_E130_k3_F128_zipf", T=1030, d=256, E=130, num_local=130, k=3,
+        F=128, seed=32),
     # f32 with more tiles than the tiny workload
     "f32_tiles": synth.WORKLOADS["tiny"].replace(
         name="f32_T300_d256_E8_k3_F384", T=300, d=256, E=8, num_local=8, k=3, F=384, seed=26),
@@ -284,7 +292,8 @@ def test_standalone_calls_match_forward():
     logits = torch.empty((T, E), dtype=torch.float32, device=DEV)
     idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
     gw = torch.empty((T, k), dtype=torch.float32, device=DEV)
-    B.moe_route(p, g["x"], g["w_router"], g["bias"], logits, idx, gw)
+    B.moe_route(p, g["x"], g["w_router"], g["bias"], logits, idx, gw,
+                B.workspace(p, B.MOE_CALL_ROUTE, DEV))
     counts = torch.empty((El,), dtype=torch.int32, device=DEV)
     offsets = torch.empty((El + 1,), dtype=torch.int32, device=DEV)
     ss = torch.empty((T * k,), dtype=torch.int32, device=DEV)
