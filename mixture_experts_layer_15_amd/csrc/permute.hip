@@ -10,8 +10,9 @@
 //   1. hist:    each workgroup counts the kept slots of its 2048-slot chunk per
 //               local expert (LDS counters; counting is order-free).
 //   2. scan:    one workgroup sums the chunk counts per expert, scans them into
-//               `offsets`, and turns the chunk counts into each chunk's first
-//               position inside every expert segment.
+//               `offsets`, turns the chunk counts into each chunk's first
+//               position inside every expert segment, and writes the expert
+//               GEMM's tile schedule.
 //   3. scatter: each workgroup walks its chunk in slot order, 256 slots per
 //               round; a slot's rank among equal experts inside its wave comes
 //               from ballots over the expert id bits, across waves from
@@ -48,22 +49,42 @@ __global__ __launch_bounds__(kThreads) void permute_hist_kernel(const int32_t* _
   for (int e = threadIdx.x; e < El; e += kThreads) blk_cnt[(size_t)e * nb + b] = hist[e];
 }
 
-// One workgroup of kMaxExperts threads: thread e owns local expert e.
+// One workgroup of kMaxExperts threads: thread e owns local expert e.  The
+// chunk counts are staged through LDS with coalesced loads and stores when
+// they fit (rows padded by one word against bank conflicts).  With `tiles`,
+// it also writes the expert GEMM's tile schedule (the M tiles of every expert
+// segment), which saves the schedule kernel.
+constexpr int kScanLds = 12288;  // staged counts (48 KB)
+
 __global__ __launch_bounds__(kMaxExperts) void permute_scan_kernel(int El, int nb, int32_t* blk,
                                                                    int32_t* counts,
-                                                                   int32_t* offsets) {
+                                                                   int32_t* offsets, int bm,
+                                                                   int4* tiles, int* ntiles) {
   __shared__ int sums[kMaxExperts];
+  __shared__ int tsum[kMaxExperts];
+  __shared__ int stage[kScanLds];
   const int e = threadIdx.x;
+  const int pitch = nb + 1;
+  const bool staged = (long long)El * pitch <= kScanLds;
+  if (staged) {
+    for (int i = e; i < El * nb; i += kMaxExperts) stage[(i / nb) * pitch + i % nb] = blk[i];
+    __syncthreads();
+  }
+  auto at = [&](int b) -> int& { return staged ? stage[e * pitch + b] : blk[(size_t)e * nb + b]; };
   int cnt = 0;
   if (e < El)
-    for (int b = 0; b < nb; ++b) cnt += blk[(size_t)e * nb + b];
+    for (int b = 0; b < nb; ++b) cnt += at(b);
+  const int nt = (tiles && e < El) ? (cnt + bm - 1) / bm : 0;
   sums[e] = cnt;
+  tsum[e] = nt;
   __syncthreads();
-  // inclusive Hillis-Steele scan over the experts
+  // inclusive Hillis-Steele scans over the experts (slots and M tiles)
   for (int o = 1; o < kMaxExperts; o <<= 1) {
     const int v = e >= o ? sums[e - o] : 0;
+    const int u = e >= o ? tsum[e - o] : 0;
     __syncthreads();
     sums[e] += v;
+    tsum[e] += u;
     __syncthreads();
   }
   const int excl = sums[e] - cnt;
@@ -72,12 +93,21 @@ __global__ __launch_bounds__(kMaxExperts) void permute_scan_kernel(int El, int n
     offsets[e] = excl;
     int run = excl;
     for (int b = 0; b < nb; ++b) {
-      const int c = blk[(size_t)e * nb + b];
-      blk[(size_t)e * nb + b] = run;
+      const int c = at(b);
+      at(b) = run;
       run += c;
     }
+    const int tfirst = tsum[e] - nt;
+    for (int i = 0; i < nt; ++i) tiles[tfirst + i] = make_int4(e, excl + i * bm, excl + cnt, 0);
   }
-  if (e == El - 1) offsets[El] = sums[e];
+  if (e == El - 1) {
+    offsets[El] = sums[e];
+    if (tiles) *ntiles = tsum[e];
+  }
+  if (staged) {
+    __syncthreads();
+    for (int i = e; i < El * nb; i += kMaxExperts) blk[i] = stage[(i / nb) * pitch + i % nb];
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void permute_scatter_kernel(
@@ -241,12 +271,15 @@ hipError_t permute(const Shape& s, const int32_t* topk_idx, int32_t* counts, int
                        s.El, nb, blk);
   }
   hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kMaxExperts), 0, st, s.El, nb, blk, counts,
-                     offsets);
+                     offsets, sched ? sched->bm : 1, sched ? sched->tiles : nullptr,
+                     sched ? sched->ntiles : nullptr);
   if (nb > 0) {
     hipLaunchKernelGGL(permute_scatter_kernel, dim3(nb), dim3(kThreads), 0, st, topk_idx, s.S,
                        s.e0, s.El, nbits, nb, blk, sorted_slot, slot_pos);
   }
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && sched_written) *sched_written = sched != nullptr;
+  return e;
 }
 
 }  // namespace moe
