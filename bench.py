@@ -75,21 +75,25 @@ def expert_bytes(d: int, F: int, wfmt: str, n_experts: int, with_scales: bool = 
     return b
 
 
-def algorithmic(wl: synth.Workload, counts: np.ndarray) -> dict:
-    """Algorithmic FLOPs and HBM bytes of one layer step and of the gate/up GEMM."""
+def algorithmic(wl: synth.Workload, counts: np.ndarray, tokens_read: int) -> dict:
+    """Algorithmic FLOPs and HBM bytes of one layer step and of the gate/up GEMM:
+    the touched local experts' weights (and FP8 scales) once, the router matrix
+    (when routing is part of the share), the token rows that have a local slot
+    once, and the output once; FLOPs 2 T d E (router) + 6 N d F."""
     d, F, E, T, k = wl.d, wl.F, wl.E, wl.T, wl.k
     ab, wb = ACT_BYTES[wl.act], W_BYTES[wl.weight]
     N = int(counts.sum())
     touched = int((counts > 0).sum())
-    tokens_read = T  # every token row is read once (all of them are routed)
-    router = 2 * T * d * E
-    layer_flop = router + 6 * N * d * F
-    layer_bytes = (expert_bytes(d, F, wl.weight, touched) + d * E * ab + T * E * 4
-                   + tokens_read * d * ab + T * d * ab)
+    router_flop = 2 * T * d * E
+    router_bytes = d * E * ab
+    expert_flop = 6 * N * d * F
+    expert_bytes_ = expert_bytes(d, F, wl.weight, touched) + tokens_read * d * ab + T * d * ab
     gu_flop = 4 * N * d * F
     gu_scales = 2 * (d // 128) * (F // 128) * 4 if wl.weight == "fp8" else 0
     gu_bytes = touched * (2 * d * F * wb + gu_scales) + tokens_read * d * ab + N * F * ab
-    return dict(N=N, touched=touched, layer_flop=layer_flop, layer_bytes=layer_bytes,
+    return dict(N=N, touched=touched, tokens_read=tokens_read,
+                layer_flop=router_flop + expert_flop, layer_bytes=router_bytes + expert_bytes_,
+                expert_flop=expert_flop, expert_bytes=expert_bytes_,
                 gu_flop=gu_flop, gu_bytes=gu_bytes, gu_unit_bytes=2 * d * F * wb + gu_scales)
 
 
@@ -167,9 +171,124 @@ def cpu_baseline(pr: synth.Problem, logits: torch.Tensor, budget_s: float) -> di
             break
     what = (f"{reps} whole step(s) of T={wl.T}" if sample is None else
             f"{reps} x 64 sampled tokens of T={wl.T} (routing of all T each time)")
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:  # pragma: no cover
+        pass
     return {"value": n_tok / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": what, "seconds": round(el, 2),
-            "host_cpus": len(os.sched_getaffinity(0))}
+            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": model,
+            "blas_threads": int(threads)}
+
+
+def measure(wl: synth.Workload, steps: int, warmup: int, copies: int, dev) -> dict:
+    """Time `steps` moe_forward calls (after `warmup`) rotating `copies` weight
+    copies, then the same steps with the library's stage events, then a warm
+    pass on one copy.  Returns times and the routing statistics."""
+    pr = synth.make_problem(wl)
+    p = B.problem(wl.T, wl.d, wl.E, wl.k, wl.F, wl.expert_begin, wl.num_local, wl.act, wl.weight)
+    x = pr.x.to(dev)
+    wr = pr.w_router.to(dev)
+    bias = None if pr.bias is None else pr.bias.to(dev)
+    wsets = []
+    for c in range(copies):
+        wsets.append({n: (None if getattr(pr, n) is None else getattr(pr, n).to(dev))
+                      for n in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")})
+    out = torch.empty((wl.T, wl.d), dtype=pr.x.dtype, device=dev)
+    logits = torch.empty((wl.T, wl.E), dtype=torch.float32, device=dev)
+    counts = torch.empty((wl.num_local,), dtype=torch.int32, device=dev)
+    slot_pos = torch.empty((wl.T * wl.k,), dtype=torch.int32, device=dev)
+    ws = B.workspace(p, B.MOE_CALL_FORWARD, dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i: int, events=None) -> None:
+        w = wsets[i % copies]
+        B.moe_forward(p, x=x, w_router=wr, router_bias=bias, w_gate=w["w_gate"], w_up=w["w_up"],
+                      w_down=w["w_down"], s_gate=w["s_gate"], s_up=w["s_up"], s_down=w["s_down"],
+                      out=out, ws=ws, logits=logits, counts=counts, slot_pos=slot_pos,
+                      events=events, stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print(f"[bench] {wl.name}: warmup {warmup} done, timing {steps} steps ({copies} weight "
+          "copies)", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
+
+    # Stage times: the same steps again, with HIP events recorded by the library
+    # on its stream at every stage boundary.
+    ev_sets = [HipEvents(B.MOE_FORWARD_EVENTS) for _ in range(steps)]
+    for i in range(steps):
+        step(i, ev_sets[i].arr)
+    torch.cuda.synchronize()
+    names = ["route", "permute", "schedule", "gate_up", "down", "combine"]
+    stage = {n: [] for n in names}
+    layer_ev = []
+    for e in ev_sets:
+        e.sync(6)
+        for s_i, n in enumerate(names):
+            stage[n].append(e.ms(s_i, s_i + 1))
+        layer_ev.append(e.ms(0, 6))
+    stage_ms = {n: float(np.mean(v)) for n, v in stage.items()}
+    share_ev = [l - r for l, r in zip(layer_ev, stage["route"])]  # permute .. combine
+
+    # warm: one weight copy, so that the Infinity Cache may serve part of it (info)
+    warm_steps = max(steps // 2, 5)
+    for i in range(3):
+        step(0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(warm_steps):
+        step(0)
+    torch.cuda.synchronize()
+    warm_ms = (time.perf_counter() - t0) * 1e3 / warm_steps
+
+    sp = slot_pos.cpu().numpy().reshape(wl.T, wl.k)
+    tokens_read = int((sp >= 0).any(axis=1).sum())
+    return dict(pr=pr, logits=logits, counts=counts.cpu().numpy(), tokens_read=tokens_read,
+                ms_per_step=ms_per_step, stage_ms=stage_ms, layer_ev=layer_ev, share_ev=share_ev,
+                warm_ms=warm_ms, copies=copies)
+
+
+def pct(v, q) -> float:
+    return round(float(np.percentile(np.asarray(v), q)), 5)
+
+
+def sweep(args, dev) -> None:
+    """Batch sweep at the Qwen3-30B-A3B shape: as T grows, the experts touched
+    (hence the weight bytes) saturate while the FLOPs keep growing, and the
+    layer moves from the HBM roofline to the MFMA one.  One JSON line per T."""
+    base = synth.WORKLOADS["decode"]
+    for T in [int(t) for t in args.sweep.split(",")]:
+        wl = base.replace(name=f"qwen3_30b_a3b_T{T}_d2048_E128_k8_F768", T=T)
+        steps = args.steps or (100 if T <= 512 else 20)
+        m = measure(wl, steps, args.warmup if args.warmup is not None else 5, 4, dev)
+        alg = algorithmic(wl, m["counts"], m["tokens_read"])
+        t = m["ms_per_step"] * 1e-3
+        gu = m["stage_ms"]["gate_up"] * 1e-3
+        print(json.dumps({
+            "sweep": "qwen3_30b_a3b_batch", "T": T, "touched_experts": alg["touched"],
+            "kept_slots": alg["N"], "ms_per_step": round(m["ms_per_step"], 5),
+            "tokens_per_s": round(T / t, 1),
+            "layer": {"alg_bytes": alg["layer_bytes"], "alg_flop": alg["layer_flop"],
+                      "gbs": round(alg["layer_bytes"] / t / 1e9, 1),
+                      "frac_hbm": round(alg["layer_bytes"] / t / 1e9 / PEAK_HBM_GBS, 4),
+                      "tflops": round(alg["layer_flop"] / t / 1e12, 2),
+                      "frac_mfma_bf16": round(alg["layer_flop"] / t / 1e12 / PEAK_BF16_TFLOPS, 4),
+                      "flop_per_byte": round(alg["layer_flop"] / alg["layer_bytes"], 1)},
+            "gate_up": {"ms": round(m["stage_ms"]["gate_up"], 5),
+                        "gbs": round(alg["gu_bytes"] / gu / 1e9, 1),
+                        "tflops": round(alg["gu_flop"] / gu / 1e12, 2)},
+            "stage_ms": {n: round(v, 5) for n, v in m["stage_ms"].items()},
+        }), flush=True)
 
 
 def main() -> None:
@@ -181,6 +300,9 @@ def main() -> None:
     ap.add_argument("--weight-copies", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", default=None,
+                    help="comma-separated token counts: batch sweep at the Qwen3 shape "
+                         "(one JSON line per T instead of the bench line)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the MoE layer: only --gpus 1 is supported "
@@ -189,67 +311,22 @@ def main() -> None:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    dev = torch.device("cuda:0")
+    B.load_library()
+    if args.sweep:
+        sweep(args, dev)
+        return
 
     wl = synth.WORKLOADS[args.config]
     steps = args.steps or (200 if wl.regime in ("decode", "tiny") else 50)
     warmup = args.warmup if args.warmup is not None else 10
-    dev = torch.device("cuda:0")
-    B.load_library()
-    pr = synth.make_problem(wl)
-    p = B.problem(wl.T, wl.d, wl.E, wl.k, wl.F, wl.expert_begin, wl.num_local, wl.act, wl.weight)
-
-    wbytes = expert_bytes(wl.d, wl.F, wl.weight, wl.num_local)
-    copies = args.weight_copies or max(2, min(8, -(-1024 ** 3 // wbytes) + 1))
-    x = pr.x.to(dev)
-    wr = pr.w_router.to(dev)
-    bias = None if pr.bias is None else pr.bias.to(dev)
-    wsets = []
-    for c in range(copies):
-        wsets.append({n: (None if getattr(pr, n) is None else getattr(pr, n).to(dev))
-                      for n in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")})
-    out = torch.empty((wl.T, wl.d), dtype=pr.x.dtype, device=dev)
-    logits = torch.empty((wl.T, wl.E), dtype=torch.float32, device=dev)
-    counts = torch.empty((wl.num_local,), dtype=torch.int32, device=dev)
-    ws = B.workspace(p, B.MOE_CALL_FORWARD, dev)
-    stream = torch.cuda.current_stream()
-
-    def step(i: int, events=None) -> None:
-        w = wsets[i % copies]
-        B.moe_forward(p, x=x, w_router=wr, router_bias=bias, w_gate=w["w_gate"], w_up=w["w_up"],
-                      w_down=w["w_down"], s_gate=w["s_gate"], s_up=w["s_up"], s_down=w["s_down"],
-                      out=out, ws=ws, logits=logits, counts=counts, events=events, stream=stream)
-
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    print(f"[bench] {wl.name}: warmup {warmup} done, timing {steps} steps", file=sys.stderr,
-          flush=True)
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(i)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / steps
-
-    # Stage times: the same steps again, with HIP events recorded by the library
-    # on its stream at every stage boundary.
-    ev_sets = [HipEvents(B.MOE_FORWARD_EVENTS) for _ in range(steps)]
-    for i in range(steps):
-        step(i, ev_sets[i].arr)
-    torch.cuda.synchronize()
-    names = ["route", "permute", "schedule", "gate_up", "down", "combine"]
-    stage_ms = {n: 0.0 for n in names}
-    layer_ev_ms = 0.0
-    for e in ev_sets:
-        e.sync(6)
-        for s_i, n in enumerate(names):
-            stage_ms[n] += e.ms(s_i, s_i + 1)
-        layer_ev_ms += e.ms(0, 6)
-    stage_ms = {n: v / steps for n, v in stage_ms.items()}
-    layer_ev_ms /= steps
-
-    cnt = counts.cpu().numpy()
-    alg = algorithmic(wl, cnt)
+    # at least four weight copies rotate through the steps, so that no step
+    # finds a previous step's weights in the 256 MB Infinity Cache
+    copies = args.weight_copies or 4
+    m = measure(wl, steps, warmup, copies, dev)
+    pr, cnt = m["pr"], m["counts"]
+    alg = algorithmic(wl, cnt, m["tokens_read"])
+    ms_per_step, stage_ms = m["ms_per_step"], m["stage_ms"]
     t_layer = ms_per_step * 1e-3
     t_gu = stage_ms["gate_up"] * 1e-3
     decode = wl.regime in ("decode", "tiny")
@@ -270,6 +347,28 @@ def main() -> None:
     roof["bytes_per_launch"] = alg["gu_bytes"]
     roof["flop_per_launch"] = alg["gu_flop"]
 
+    layer = {"tflops": round(alg["layer_flop"] / t_layer / 1e12, 2),
+             "gbs": round(alg["layer_bytes"] / t_layer / 1e9, 1),
+             "frac_hbm": round(alg["layer_bytes"] / t_layer / 1e9 / PEAK_HBM_GBS, 4),
+             "frac_mfma_bf16": round(alg["layer_flop"] / t_layer / 1e12 / PEAK_BF16_TFLOPS, 4),
+             "kept_slots": alg["N"], "kept_slots_per_s": round(alg["N"] / t_layer, 1),
+             "touched_experts": alg["touched"], "tokens_with_local_slot": alg["tokens_read"],
+             "max_over_mean_load": round(float(cnt.max() / max(cnt.mean(), 1e-9)), 2),
+             "stage_ms": {n: round(v, 5) for n, v in stage_ms.items()},
+             "event_ms_per_step": {"p10": pct(m["layer_ev"], 10), "p50": pct(m["layer_ev"], 50),
+                                   "p90": pct(m["layer_ev"], 90)},
+             "warm_ms_per_step": round(m["warm_ms"], 5)}
+    if wl.num_local < wl.E:
+        # one expert-parallel rank's share: routing all T tokens over all E
+        # experts is setup shared by the ranks; the share is permute .. combine
+        t_share = float(np.median(m["share_ev"])) * 1e-3
+        layer["rank_share"] = {
+            "ms_p50": round(t_share * 1e3, 5), "tokens_per_s": round(wl.T / t_share, 1),
+            "kept_slots_per_s": round(alg["N"] / t_share, 1),
+            "tflops": round(alg["expert_flop"] / t_share / 1e12, 2),
+            "gbs": round(alg["expert_bytes"] / t_share / 1e9, 1),
+            "frac_mfma_bf16": round(alg["expert_flop"] / t_share / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
     result = {
         "metric": METRIC,
         "value": round(wl.T / t_layer, 1),
@@ -288,19 +387,12 @@ def main() -> None:
                    "act": wl.act, "weights": wl.weight, "weight_copies": copies,
                    "parallelism": "single GPU (all experts local)" if wl.num_local == wl.E
                    else "one expert-parallel rank's expert block"},
-        "layer": {"tflops": round(alg["layer_flop"] / t_layer / 1e12, 2),
-                  "gbs": round(alg["layer_bytes"] / t_layer / 1e9, 1),
-                  "frac_hbm": round(alg["layer_bytes"] / t_layer / 1e9 / PEAK_HBM_GBS, 4),
-                  "frac_mfma_bf16": round(alg["layer_flop"] / t_layer / 1e12 / PEAK_BF16_TFLOPS, 4),
-                  "kept_slots": alg["N"], "touched_experts": alg["touched"],
-                  "max_over_mean_load": round(float(cnt.max() / max(cnt.mean(), 1e-9)), 2),
-                  "stage_ms": {n: round(v, 5) for n, v in stage_ms.items()},
-                  "event_ms_per_step": round(layer_ev_ms, 5)},
+        "layer": layer,
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(pr, logits, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(pr, m["logits"], args.cpu_budget)
     print(json.dumps(result), flush=True)
 
 

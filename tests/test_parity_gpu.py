@@ -338,6 +338,17 @@ def _sample(T, n, seed):
     return np.sort(rng.choice(T, size=min(n, T), replace=False))
 
 
+@pytest.mark.parametrize("T", [1, 2, 4, 16, 64, 256, 1024, 4096])
+def test_batch_sweep_parity(T):
+    """The Qwen3-shaped layer across the batch sizes of the sweep (the decode
+    workload's distributions with T tokens): every tile plan from decode to
+    prefill tiles, on a sample of tokens at the larger sizes."""
+    wl = synth.WORKLOADS["decode"].replace(name=f"qwen3_sweep_T{T}", T=T, seed=70 + T % 97)
+    pr = synth.make_problem(wl)
+    gpu = forward(pr)
+    check(pr, gpu, tokens=None if T <= 64 else _sample(T, 24, seed=T))
+
+
 @pytest.mark.parametrize("name,n_sample", [("decode", None), ("prefill", 96), ("mixtral", 32),
                                            ("dsv3_rank", 48)])
 def test_full_size_workloads(name, n_sample):
