@@ -46,15 +46,18 @@ W_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
 
 def gate_up_kernel_name(wl: synth.Workload) -> str:
     """The gate/up kernel the library launches for this workload, as a
-    rocprofv3 kernel trace names it (the library's tile plan: decode tiles when
-    an expert averages at most 64 slots, then FP8, then 256x256 tiles from
-    1024 slots per expert, else 128x512)."""
+    rocprofv3 kernel trace names it (the library's tile plan: 32-row decode
+    tiles up to 16 slots per expert on average, 64-row ones up to 64 (FP8: the
+    32-row ones), then FP8, then 256x256 tiles from 1024 slots per expert, else
+    128x512)."""
     S, El = wl.T * wl.k, wl.num_local
     if wl.weight == "f32":
         return "grouped_f32_kernel<true>"
     fp8 = str(wl.weight == "fp8").lower()
-    if S <= 64 * El:
+    if S <= 16 * El or (S <= 64 * El and wl.weight == "fp8"):
         args = f"1, 1, 2, 4, true, {fp8}, 64, 4, {2 if wl.weight == 'fp8' else 1}"
+    elif S <= 64 * El:
+        args = "2, 1, 2, 4, true, false, 64, 4, 1"
     elif wl.weight == "fp8":
         args = "2, 2, 4, 4, true, true, 64, 3, 1"
     elif S >= 1024 * El:

@@ -761,27 +761,33 @@ hipError_t launch_gemm(const GemmArgs& a, long long max_items, hipStream_t st) {
 }
 
 // Tile plans.  Decode (a handful of rows per expert): 32 x 256 tiles, four
-// waves side by side along N, 64-deep K steps, 4 stages.  bf16 prefill: eight
+// waves side by side along N, 64-deep K steps, 4 stages; from 17 to 64 rows
+// per expert on average (bf16), 64 x 256 tiles, so that an expert's weights
+// are streamed by one M tile instead of two or three.  bf16 prefill: eight
 // waves of 64 x 128, 32-deep K steps and 4 stages, as 128 x 512 tiles when
 // experts hold a few hundred rows (less M padding) or 256 x 256 when they hold
 // a thousand or more (fewer bytes staged per MFMA).  FP8 weights: eight waves
 // of 64 x 128 in 128 x 512 tiles, 64-deep K steps (one byte per code) and 3
 // stages.
-enum class Plan { kF32, kDecode, kWide, kBig, kFp8 };
+enum class Plan { kF32, kDecode, kDecode64, kWide, kBig, kFp8 };
 
 Plan plan_of(const Shape& s) {
   if (s.weight == kF32) return Plan::kF32;
-  if (s.S <= 64LL * s.El) return Plan::kDecode;
+  if (s.S <= 16LL * s.El) return Plan::kDecode;
+  if (s.S <= 64LL * s.El) return s.weight == kFP8 ? Plan::kDecode : Plan::kDecode64;
   if (s.weight == kFP8) return Plan::kFp8;
   return s.S >= 1024LL * s.El ? Plan::kBig : Plan::kWide;
 }
 
-bool use_decode_tiles(const Shape& s) { return plan_of(s) == Plan::kDecode; }
+bool use_decode_tiles(const Shape& s) {
+  return plan_of(s) == Plan::kDecode || plan_of(s) == Plan::kDecode64;
+}
 
 int tile_bm(const Shape& s) {
   switch (plan_of(s)) {
     case Plan::kF32: return kF32BM;
     case Plan::kDecode: return 32;
+    case Plan::kDecode64: return 64;
     case Plan::kBig: return 256;
     default: return 128;
   }
@@ -913,6 +919,13 @@ hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
         if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
         if (e == hipSuccess) e = launch_gemm<1, 1, 2, 4, false, false, 64, 4, 1>(dn, mt * dn.n_tiles_n, st);
       }
+      break;
+    case Plan::kDecode64:
+      gu.n_tiles_n = ntn(s.F, 128);
+      dn.n_tiles_n = ntn(s.d, 256);
+      e = launch_gemm<2, 1, 2, 4, true, false, 64, 4, 1>(gu, mt * gu.n_tiles_n, st);
+      if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
+      if (e == hipSuccess) e = launch_gemm<2, 1, 2, 4, false, false, 64, 4, 1>(dn, mt * dn.n_tiles_n, st);
       break;
     case Plan::kFp8:
       gu.n_tiles_n = ntn(s.F, 256);

@@ -169,6 +169,8 @@ def test_small_full_parity(case):
 # Capping the persistent grid at 8 workgroups gives each workgroup many items.
 MULTI = {
     "decode_plan": synth.WORKLOADS["decode"].replace(
+        name="bf16_T40_d512_E16_k4_F512", T=40, d=512, E=16, num_local=16, k=4, F=512, seed=60),
+    "decode64_plan": synth.WORKLOADS["decode"].replace(
         name="bf16_T96_d512_E16_k4_F512", T=96, d=512, E=16, num_local=16, k=4, F=512, seed=61),
     "wide_plan": synth.WORKLOADS["prefill"].replace(
         name="bf16_T900_d512_E8_k2_F384_zipf", T=900, d=512, E=8, num_local=8, k=2, F=384,
