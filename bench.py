@@ -64,7 +64,7 @@ def gate_up_kernel_name(wl: synth.Workload) -> str:
         args = "2, 4, 4, 2, true, false, 32, 4, 1"
     else:
         args = "2, 2, 4, 4, true, false, 32, 4, 1"
-    return f"grouped_gemm_kernel<{args}>"
+    return f"grouped_gemm_kernel<{args}, false>"
 
 
 def expert_bytes(d: int, F: int, wfmt: str, n_experts: int, with_scales: bool = True) -> int:
