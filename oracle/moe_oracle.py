@@ -58,7 +58,7 @@ __all__ = [
     "bf16_bits_to_f64", "e4m3fn_table", "e4m3fn_to_f64", "dequant_block128",
     "decode_act", "decode_expert_weight", "router_logits", "topk_select",
     "renormalised_gates", "local_slot_mask", "expert_permutation",
-    "silu", "swiglu_ffn", "moe_layer_forward", "brute_force_dense",
+    "silu", "swiglu_ffn", "moe_layer_forward", "routed_layer_forward", "brute_force_dense",
 ]
 
 BLOCK = 128  # side of the square fp8 scale block
@@ -278,13 +278,24 @@ def moe_layer_forward(x, logits, k, w_gate, w_up, w_down, *, act_fmt, weight_fmt
     ``offsets``, ``sorted_slot``, ``slot_pos`` and ``out`` (float64 rows for
     ``tokens``, or all T rows), plus ``tokens``.
     """
-    x64_all = None
     L = np.asarray(logits)
     T, E = L.shape
     if E_l is None:
         E_l = E - e0
     idx = topk_select(L, k)
     w = renormalised_gates(L, idx)
+    return routed_layer_forward(x, idx, w, w_gate, w_up, w_down, act_fmt=act_fmt,
+                                weight_fmt=weight_fmt, e0=e0, E_l=E_l, s_gate=s_gate, s_up=s_up,
+                                s_down=s_down, tokens=tokens)
+
+
+def routed_layer_forward(x, idx, w, w_gate, w_up, w_down, *, act_fmt, weight_fmt, e0, E_l,
+                         s_gate=None, s_up=None, s_down=None, tokens=None):
+    """The layer's dispatch, experts and combine for given routing: expert ids
+    ``idx [T, k]`` (ids outside the block ``[e0, e0+E_l)`` are not local) and
+    gates ``w [T, k]``.  Same outputs as ``moe_layer_forward``."""
+    x64_all = None
+    T, k = idx.shape
     counts, offsets, sorted_slot, slot_pos = expert_permutation(idx, e0, E_l)
 
     tok = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
