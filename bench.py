@@ -294,6 +294,125 @@ def sweep(args, dev) -> None:
         }), flush=True)
 
 
+def eplb(args, dev) -> None:
+    """Expert-parallel load balancing at the DeepSeek-V3 shape (T = 16384,
+    d = 7168, E = 256, k = 8, F = 2048, FP8 weights, Zipf-skewed router) on
+    G = 8 ranks ("Serving MoE models with expert parallelism on 8xH200",
+    section "Routing imbalance": copies of hot experts on less-loaded GPUs).
+
+    The plan is made from the per-expert counts of one batch (the window) and
+    measured on another batch of the same traffic.  Every rank's share
+    (dispatch, expert FFN on its physical slots, combine) runs on this GPU,
+    one rank after another, timed with events on the library's stream; with
+    the ranks running side by side the layer waits for the slowest one.  The
+    rank weights are random experts of the workload's shape (the kernels'
+    time does not depend on their values; the copies' parity is tested
+    separately).  One JSON line per placement."""
+    G = 8
+    base = synth.WORKLOADS["dsv3_rank"]
+    Rs = [int(r) for r in args.eplb.split(",")]
+    S_max = (base.E + max(Rs)) // G
+    wl = base.replace(name="deepseek_v3_T16384_d7168_E256_k8_F2048_fp8_zipf1.2", num_local=S_max)
+    pr = synth.make_problem(wl)
+    x_meas = pr.x.to(dev)
+    x_win = synth.tokens(wl, seed=1000 + wl.seed).to(dev)
+    wr = pr.w_router.to(dev)
+    bias = pr.bias.to(dev)
+    W = {n: getattr(pr, n).to(dev) for n in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")}
+    T, d, E, k, F = wl.T, wl.d, wl.E, wl.k, wl.F
+    stream = torch.cuda.current_stream()
+
+    def route(x):
+        p = B.problem(T, d, E, k, F, 0, E, wl.act, wl.weight)
+        logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+        idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        gw = torch.empty((T, k), dtype=torch.float32, device=dev)
+        B.moe_route(p, x, wr, bias, logits, idx, gw, ws=B.workspace(p, B.MOE_CALL_ROUTE, dev))
+        counts = torch.empty((E,), dtype=torch.int32, device=dev)
+        offs = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+        srt = torch.empty((T * k,), dtype=torch.int32, device=dev)
+        pos = torch.empty((T * k,), dtype=torch.int32, device=dev)
+        B.moe_permute(p, idx, counts, offs, srt, pos, B.workspace(p, B.MOE_CALL_PERMUTE, dev))
+        torch.cuda.synchronize()
+        return idx, gw, counts.cpu().numpy().astype(np.int64)
+
+    _, _, window_load = route(x_win)
+    idx, gw, meas_load = route(x_meas)
+    print(f"[bench] eplb: routed window and measured batches; window max/mean expert load "
+          f"{window_load.max() / window_load.mean():.2f}", file=sys.stderr, flush=True)
+    y = torch.empty((T * k, d), dtype=pr.x.dtype, device=dev)
+    out = torch.empty((T, d), dtype=pr.x.dtype, device=dev)
+    steps, warmup = args.steps or 5, args.warmup if args.warmup is not None else 2
+
+    def rank_ms(ids, P, S, g):
+        p = B.problem(T, d, P, k, F, g * S, S, wl.act, wl.weight)
+        counts = torch.empty((S,), dtype=torch.int32, device=dev)
+        offs = torch.empty((S + 1,), dtype=torch.int32, device=dev)
+        srt = torch.empty((T * k,), dtype=torch.int32, device=dev)
+        pos = torch.empty((T * k,), dtype=torch.int32, device=dev)
+        wsp = B.workspace(p, B.MOE_CALL_PERMUTE, dev)
+        wsf = B.workspace(p, B.MOE_CALL_EXPERT_FFN, dev)
+
+        def share():
+            B.moe_permute(p, ids, counts, offs, srt, pos, wsp, stream=stream)
+            B.moe_expert_ffn(p, x_meas, srt, offs, W["w_gate"], W["w_up"], W["w_down"],
+                             W["s_gate"], W["s_up"], W["s_down"], gw, y, wsf, stream=stream)
+            B.moe_combine(p, y, pos, None, out, stream=stream)
+
+        for _ in range(warmup):
+            share()
+        ts = []
+        for _ in range(steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            share()
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts)), int(counts.sum().item())
+
+    base_max = None
+    for label, R in [("contiguous", None)] + [(f"eplb_R{r}", r) for r in Rs]:
+        if R is None:
+            P, S = E, E // G
+            ids, rep_plan, remap_ms = idx, None, 0.0
+            planned = None
+        else:
+            P, S = E + R, (E + R) // G
+            t0 = time.perf_counter()
+            rep, p2l, l2p, rl = B.moe_eplb_plan(window_load, G, R)
+            plan_ms = (time.perf_counter() - t0) * 1e3
+            ids = torch.empty_like(idx)
+            d_rep = torch.from_numpy(rep).to(dev)
+            d_l2p = torch.from_numpy(l2p).to(dev)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            B.moe_eplb_remap(T, k, E, G, idx, d_rep, d_l2p, ids, stream=stream)
+            a.record(stream)
+            B.moe_eplb_remap(T, k, E, G, idx, d_rep, d_l2p, ids, stream=stream)
+            b.record(stream)
+            b.synchronize()
+            remap_ms = a.elapsed_time(b)
+            rep_plan = {"max_copies": int(rep.max()), "experts_copied": int((rep > 1).sum()),
+                        "plan_ms_host": round(plan_ms, 3)}
+            planned = float(rl.max() / rl.mean())
+        per = [rank_ms(ids, P, S, g) for g in range(G)]
+        ms = [m for m, _ in per]
+        slots = [c for _, c in per]
+        base_max = max(ms) if base_max is None else base_max
+        line = {"eplb": label, "workload": wl.name, "ranks": G, "redundant_experts": R or 0,
+                "slots_per_rank": S, "rank_slots": slots,
+                "imbalance_slots": round(max(slots) / (sum(slots) / G), 4),
+                "imbalance_planned": None if planned is None else round(planned, 4),
+                "rank_ms": [round(m, 4) for m in ms], "max_rank_ms": round(max(ms), 4),
+                "mean_rank_ms": round(float(np.mean(ms)), 4),
+                "imbalance_time": round(max(ms) / float(np.mean(ms)), 4),
+                "tokens_per_s_slowest_rank": round(T / (max(ms) * 1e-3), 1),
+                "speedup_vs_contiguous": round(base_max / max(ms), 4),
+                "remap_ms": round(remap_ms, 5), "plan": rep_plan,
+                "steps_per_rank": steps}
+        print(json.dumps(line), flush=True)
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -303,6 +422,9 @@ def main() -> None:
     ap.add_argument("--weight-copies", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eplb", default=None,
+                    help="comma-separated redundant-expert counts: EPLB placements of the "
+                         "DeepSeek-V3 layer on 8 ranks (one JSON line per placement)")
     ap.add_argument("--sweep", default=None,
                     help="comma-separated token counts: batch sweep at the Qwen3 shape "
                          "(one JSON line per T instead of the bench line)")
@@ -318,6 +440,9 @@ def main() -> None:
     B.load_library()
     if args.sweep:
         sweep(args, dev)
+        return
+    if args.eplb:
+        eplb(args, dev)
         return
 
     wl = synth.WORKLOADS[args.config]

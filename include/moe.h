@@ -218,6 +218,58 @@ typedef struct {
 moe_status_t moe_forward(const moe_problem_t* p, const moe_forward_args_t* a, void* ws,
                          size_t ws_bytes, void* stream);
 
+/* ---- Expert-parallel load balancing (EPLB) ----
+ *
+ * "Serving MoE models with expert parallelism on 8xH200" (reviosa), section
+ * "Routing imbalance": per-expert token counts measure the load; the busiest
+ * GPU's count over the mean is the imbalance factor; hot experts get
+ * redundant copies placed on less-loaded GPUs, and co-locating hot with cold
+ * experts evens the load without copies.  The pages give no algorithm; the
+ * one here (host code, deterministic):
+ *  1. copies: P = E + R physical slots on G ranks, S = P / G per rank; each
+ *     of the R spare slots in turn goes to the expert with the largest load
+ *     per copy, load[e] / replicas[e] (exact comparison, ties to the lower
+ *     id), among experts with fewer than G copies;
+ *  2. placement: each copy carries load[e] / replicas[e] (double); copies,
+ *     heaviest first (ties: lower expert id, then lower copy index), go to
+ *     the least-loaded rank (double sum of its copies in placement order;
+ *     ties to the lower rank) among ranks with a free slot that hold no copy
+ *     of the same expert (if there is none, among ranks with a free slot);
+ *  3. numbering: rank g owns physical ids g*S .. g*S + S - 1, holding its
+ *     experts in increasing id; copy j of expert e is the j-th smallest
+ *     physical id holding e.
+ * A rank then runs moe_permute / moe_expert_ffn / moe_combine with E = P,
+ * expert_begin = g*S, num_local = S, on the ids moe_eplb_remap writes and on
+ * its physical slots' weights (copies of the logical experts' weights).  The
+ * ranks' outputs add up to the layer's output for any plan.
+ *
+ * moe_eplb_plan - host function (host pointers, nothing enqueued).
+ *  load         [E] int64, tokens routed to each expert over the caller's
+ *               window (e.g. sums of moe_permute's counts), 0 <= load < 2^40
+ *  replicas     [E] int32 output, copies per expert (1 .. G)
+ *  phys_to_log  [E + R] int32 output, logical expert of each physical slot
+ *  log_to_phys  [E][G] int32 output, physical slot of copy j of expert e
+ *               (j < replicas[e]), -1 beyond
+ *  rank_load    [G] double output or NULL, the planned load per rank
+ * Limits: 1 <= E, 1 <= G, 0 <= R <= E*(G-1), (E + R) divisible by G,
+ * E + R <= 512.  Otherwise MOE_ERR_INVALID_ARGUMENT (MOE_ERR_UNSUPPORTED for
+ * E + R > 512), with the outputs untouched. */
+moe_status_t moe_eplb_plan(const int64_t* load, int32_t E, int32_t G, int32_t R,
+                           int32_t* replicas, int32_t* phys_to_log, int32_t* log_to_phys,
+                           double* rank_load);
+
+/* moe_eplb_remap - device: logical top-k ids -> physical ids.  The slot of
+ * token t routed to expert e goes to copy (t mod replicas[e]):
+ *   topk_phys[t*k + i] = log_to_phys[e*G + t % replicas[e]],  e = topk_idx[t*k + i]
+ * and -1 (never local on any rank) for e outside [0, E) or a replicas entry
+ * outside [1, G].
+ *  topk_idx [T*k], replicas [E], log_to_phys [E*G], topk_phys [T*k]: device
+ *  arrays (topk_phys may not alias the others).  Limits: T >= 0, 1 <= k,
+ *  T*k < 2^31, 1 <= E, 1 <= G, E*G < 2^31. */
+moe_status_t moe_eplb_remap(int32_t T, int32_t k, int32_t E, int32_t G, const int32_t* topk_idx,
+                            const int32_t* replicas, const int32_t* log_to_phys,
+                            int32_t* topk_phys, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

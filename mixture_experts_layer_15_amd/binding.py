@@ -65,7 +65,12 @@ def load_library() -> ctypes.CDLL:
     lib.moe_expert_ffn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_combine.argtypes = [P, vp, vp, vp, vp, vp]
     lib.moe_forward.argtypes = [P, ctypes.POINTER(ForwardArgs), vp, sz, vp]
-    for f in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward"):
+    i64p, i32p, f64p = (ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32),
+                        ctypes.POINTER(ctypes.c_double))
+    lib.moe_eplb_plan.argtypes = [i64p, i32, i32, i32, i32p, i32p, i32p, f64p]
+    lib.moe_eplb_remap.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
+    for f in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
+              "moe_eplb_plan", "moe_eplb_remap"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -154,6 +159,32 @@ def moe_forward(p, *, x, w_router, router_bias, w_gate, w_up, w_down, out, ws,
     st = load_library().moe_forward(ctypes.byref(p), ctypes.byref(a), _ptr(ws), nbytes,
                                     _stream(stream))
     _check("moe_forward", st)
+
+
+def moe_eplb_plan(load, G: int, R: int):
+    """Host placement plan (see moe.h).  ``load``: per-expert counts (any
+    integer sequence).  Returns numpy ``(replicas [E], phys_to_log [E+R],
+    log_to_phys [E, G], rank_load [G])``."""
+    import numpy as np
+    ld = np.ascontiguousarray(np.asarray(load, dtype=np.int64))
+    E = int(ld.shape[0])
+    rep = np.zeros(E, dtype=np.int32)
+    p2l = np.zeros(max(E + R, 1), dtype=np.int32)
+    l2p = np.zeros((E, max(G, 1)), dtype=np.int32)
+    rl = np.zeros(max(G, 1), dtype=np.float64)
+    c = ctypes
+    st = load_library().moe_eplb_plan(
+        ld.ctypes.data_as(c.POINTER(c.c_int64)), E, G, R,
+        rep.ctypes.data_as(c.POINTER(c.c_int32)), p2l.ctypes.data_as(c.POINTER(c.c_int32)),
+        l2p.ctypes.data_as(c.POINTER(c.c_int32)), rl.ctypes.data_as(c.POINTER(c.c_double)))
+    _check("moe_eplb_plan", st)
+    return rep, p2l, l2p, rl
+
+
+def moe_eplb_remap(T, k, E, G, topk_idx, replicas, log_to_phys, topk_phys, stream=None) -> None:
+    st = load_library().moe_eplb_remap(T, k, E, G, _ptr(topk_idx), _ptr(replicas),
+                                       _ptr(log_to_phys), _ptr(topk_phys), _stream(stream))
+    _check("moe_eplb_remap", st)
 
 
 def workspace(p: Problem, call: int, device="cuda") -> torch.Tensor:

@@ -237,4 +237,36 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_forward_args_t* a, vo
   return from_hip(e);
 }
 
+moe_status_t moe_eplb_plan(const int64_t* load, int32_t E, int32_t G, int32_t R,
+                           int32_t* replicas, int32_t* phys_to_log, int32_t* log_to_phys,
+                           double* rank_load) {
+  if (load == nullptr || replicas == nullptr || phys_to_log == nullptr || log_to_phys == nullptr)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (E < 1 || G < 1 || R < 0 || (long long)R > (long long)E * (G - 1))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (((long long)E + R) % G != 0) return MOE_ERR_INVALID_ARGUMENT;
+  if ((long long)E + R > moe::kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  for (int e = 0; e < E; ++e)
+    if (load[e] < 0 || load[e] >= (1LL << 40)) return MOE_ERR_INVALID_ARGUMENT;
+  try {
+    moe::eplb_plan(load, E, G, R, replicas, phys_to_log, log_to_phys, rank_load);
+  } catch (const std::bad_alloc&) {
+    return MOE_ERR_UNSUPPORTED;
+  }
+  return MOE_OK;
+}
+
+moe_status_t moe_eplb_remap(int32_t T, int32_t k, int32_t E, int32_t G, const int32_t* topk_idx,
+                            const int32_t* replicas, const int32_t* log_to_phys,
+                            int32_t* topk_phys, void* stream) {
+  if (T < 0 || k < 1 || E < 1 || G < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if ((long long)T * k >= (1LL << 31) || (long long)E * G >= (1LL << 31))
+    return MOE_ERR_UNSUPPORTED;
+  if (topk_idx == nullptr || replicas == nullptr || log_to_phys == nullptr || topk_phys == nullptr)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (T == 0) return MOE_OK;
+  return from_hip(moe::eplb_remap(T, k, E, G, topk_idx, replicas, log_to_phys, topk_phys,
+                                  static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -69,4 +69,12 @@ hipError_t permute(const Shape& s, const int32_t* topk_idx, int32_t* counts, int
 hipError_t combine(const Shape& s, const void* y, const int32_t* slot_pos, const float* topk_w,
                    void* out, hipStream_t st);
 
+// ---- eplb.hip
+// The placement plan of moe_eplb_plan (arguments already checked).
+int eplb_plan(const int64_t* load, int E, int G, int R, int32_t* replicas, int32_t* phys_to_log,
+              int32_t* log_to_phys, double* rank_load);
+hipError_t eplb_remap(int T, int k, int E, int G, const int32_t* topk_idx,
+                      const int32_t* replicas, const int32_t* log_to_phys, int32_t* topk_phys,
+                      hipStream_t st);
+
 }  // namespace moe

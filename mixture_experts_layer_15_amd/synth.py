@@ -169,6 +169,14 @@ def make_problem(wl: Workload, seed: Optional[int] = None) -> Problem:
     return Problem(wl, x, w_r, bias, w_gate, w_up, w_down, s_gate, s_up, s_down)
 
 
+def tokens(wl: Workload, seed: int) -> torch.Tensor:
+    """Another batch of ``wl.T`` tokens, ``x ~ N(0, 1)`` in the activation
+    format, from its own seed (the router and experts stay those of
+    ``make_problem``): a second sample of the same traffic."""
+    rng = np.random.default_rng(seed)
+    return _store(rng.standard_normal((wl.T, wl.d), dtype=np.float32), wl.act)
+
+
 def tied_logits(T: int, E: int, levels: int, seed: int) -> torch.Tensor:
     """float32 logits ``[T, E]`` drawn from only ``levels`` distinct values, so
     that ties inside a row are frequent (for checking the lower-index rule)."""
