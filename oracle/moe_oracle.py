@@ -56,6 +56,7 @@ import numpy as np
 
 __all__ = [
     "bf16_bits_to_f64", "e4m3fn_table", "e4m3fn_to_f64", "dequant_block128",
+    "e2m1_table", "e8m0_to_f64", "dequant_mxfp4",
     "decode_act", "decode_expert_weight", "router_logits", "topk_select",
     "renormalised_gates", "local_slot_mask", "expert_permutation",
     "silu", "swiglu_ffn", "moe_layer_forward", "routed_layer_forward", "brute_force_dense",
@@ -126,6 +127,59 @@ def dequant_block128(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     return w.reshape(R, C)
 
 
+MX_BLOCK = 32  # elements sharing one E8M0 scale in an MXFP4 row
+
+
+def e2m1_table() -> np.ndarray:
+    """All 16 OCP FP4 E2M1 codes -> float64.
+
+    The format (OCP Microscaling Formats (MX) specification v1.0, FP4 E2M1
+    element): 1 sign bit (bit 3), 2 exponent bits (bits 2..1) with bias 1, 1
+    mantissa bit (bit 0); exponent field 0 encodes the subnormal ``m * 0.5``;
+    no infinity or NaN, so magnitudes run 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+    """
+    out = np.empty(16, dtype=np.float64)
+    for code in range(16):
+        sign = -1.0 if code & 0x8 else 1.0
+        e = (code >> 1) & 0x3
+        m = code & 0x1
+        out[code] = sign * (m * 0.5 if e == 0 else (1.0 + m / 2.0) * 2.0 ** (e - 1))
+    return out
+
+
+_E2M1 = e2m1_table()
+
+
+def e8m0_to_f64(s: np.ndarray) -> np.ndarray:
+    """OCP E8M0 scale bytes -> float64: ``2^(s - 127)``; 255 is NaN."""
+    s = np.asarray(s, dtype=np.int64)
+    return np.where(s == 255, np.nan, np.ldexp(1.0, s - 127))
+
+
+def dequant_mxfp4(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """One MXFP4 matrix -> float64 ``[R, C]``.
+
+    ``q [R, C/2]`` uint8: byte j of a row holds element 2j in bits 0..3 and
+    element 2j+1 in bits 4..7; ``s [C/32, R]`` uint8 E8M0 scales, stored
+    block-major (all rows' scales of K block b are contiguous);
+    ``W[r, c] = e2m1(element c of row r) * 2^(s[c // 32, r] - 127)``.
+    "Serving MoE models with expert parallelism on 8xH200": section "Memory
+    math for 8xH200" names gpt-oss-120b in its native MXFP4, section
+    "Quantization choices" 4-bit expert weights that halve the footprint of
+    FP8 again.
+    """
+    q = np.asarray(q, dtype=np.uint8)
+    R, half = q.shape
+    C = 2 * half
+    assert C % MX_BLOCK == 0 and s.shape == (C // MX_BLOCK, R)
+    codes = np.empty((R, C), dtype=np.uint8)
+    codes[:, 0::2] = q & 0x0F
+    codes[:, 1::2] = q >> 4
+    w = _E2M1[codes].reshape(R, C // MX_BLOCK, MX_BLOCK)
+    w *= e8m0_to_f64(s).T[:, :, None]   # s[c // 32, r]
+    return w.reshape(R, C)
+
+
 def decode_act(a: np.ndarray, fmt: str) -> np.ndarray:
     """Activation / router storage -> float64 (``"f32"`` or ``"bf16"`` bits)."""
     if fmt == "f32":
@@ -143,6 +197,8 @@ def decode_expert_weight(w: np.ndarray, fmt: str, scale: np.ndarray | None = Non
         return bf16_bits_to_f64(w)
     if fmt == "fp8":
         return dequant_block128(w, scale)
+    if fmt == "mxfp4":
+        return dequant_mxfp4(w, scale)
     raise ValueError(f"unknown weight format {fmt!r}")
 
 
