@@ -40,30 +40,33 @@ PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0       # dense fp8 MFMA
 PEAK_FP32_TFLOPS = 157.3       # fp32 vector / matrix
 ACT_BYTES = {"f32": 4, "bf16": 2}
-W_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
+W_BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "mxfp4": 0.5}
+W_BITS = {"f32": 32, "bf16": 16, "fp8": 8, "mxfp4": 4}
 
 
 
 def gate_up_kernel_name(wl: synth.Workload) -> str:
     """The gate/up kernel the library launches for this workload, as a
     rocprofv3 kernel trace names it (the library's tile plan: 32-row decode
-    tiles up to 16 slots per expert on average, 64-row ones up to 64 (FP8: the
-    32-row ones), then FP8, then 256x256 tiles from 1024 slots per expert, else
-    128x512)."""
+    tiles up to 16 slots per expert on average, 64-row ones up to 64 (FP8 and
+    MXFP4: the 32-row ones), then 128 x 512 tiles for FP8 and MXFP4, 256 x 256
+    from 1024 slots per expert, else 128 x 512)."""
     S, El = wl.T * wl.k, wl.num_local
     if wl.weight == "f32":
         return "grouped_f32_kernel<true>"
-    fp8 = str(wl.weight == "fp8").lower()
-    if S <= 16 * El or (S <= 64 * El and wl.weight == "fp8"):
-        args = f"1, 1, 2, 4, true, {fp8}, 64, 4, {2 if wl.weight == 'fp8' else 1}"
+    bits = W_BITS[wl.weight]
+    if wl.weight == "mxfp4":
+        args = "1, 1, 2, 4, true, 4, 64, 8, 1" if S <= 64 * El else "2, 2, 4, 4, true, 4, 64, 4, 1"
+    elif S <= 16 * El or (S <= 64 * El and wl.weight == "fp8"):
+        args = f"1, 1, 2, 4, true, {bits}, 64, 4, {2 if wl.weight == 'fp8' else 1}"
     elif S <= 64 * El:
-        args = "2, 1, 2, 4, true, false, 64, 4, 1"
+        args = "2, 1, 2, 4, true, 16, 64, 4, 1"
     elif wl.weight == "fp8":
-        args = "2, 2, 4, 4, true, true, 64, 3, 1"
+        args = "2, 2, 4, 4, true, 8, 64, 3, 1"
     elif S >= 1024 * El:
-        args = "2, 4, 4, 2, true, false, 32, 4, 1"
+        args = "2, 4, 4, 2, true, 16, 32, 4, 1"
     else:
-        args = "2, 2, 4, 4, true, false, 32, 4, 1"
+        args = "2, 2, 4, 4, true, 16, 32, 4, 1"
     return f"grouped_gemm_kernel<{args}, false>"
 
 
@@ -72,9 +75,11 @@ def expert_bytes(d: int, F: int, wfmt: str, n_experts: int, with_scales: bool = 
     bytes per parameter ("Expert Parallelism for MoE Models", section "Memory
     Sizing Equations": expert memory = experts x parameters per expert x bytes
     per parameter), plus the FP8 block scales."""
-    b = n_experts * 3 * d * F * W_BYTES[wfmt]
+    b = int(n_experts * 3 * d * F * W_BYTES[wfmt])
     if wfmt == "fp8" and with_scales:
         b += n_experts * 3 * (d // 128) * (F // 128) * 4
+    if wfmt == "mxfp4" and with_scales:
+        b += n_experts * 3 * (d * F // 32)          # one E8M0 byte per 32 weights
     return b
 
 
@@ -92,12 +97,13 @@ def algorithmic(wl: synth.Workload, counts: np.ndarray, tokens_read: int) -> dic
     expert_flop = 6 * N * d * F
     expert_bytes_ = expert_bytes(d, F, wl.weight, touched) + tokens_read * d * ab + T * d * ab
     gu_flop = 4 * N * d * F
-    gu_scales = 2 * (d // 128) * (F // 128) * 4 if wl.weight == "fp8" else 0
-    gu_bytes = touched * (2 * d * F * wb + gu_scales) + tokens_read * d * ab + N * F * ab
+    gu_scales = (2 * (d // 128) * (F // 128) * 4 if wl.weight == "fp8"
+                 else 2 * d * F // 32 if wl.weight == "mxfp4" else 0)
+    gu_bytes = int(touched * (2 * d * F * wb + gu_scales) + tokens_read * d * ab + N * F * ab)
     return dict(N=N, touched=touched, tokens_read=tokens_read,
                 layer_flop=router_flop + expert_flop, layer_bytes=router_bytes + expert_bytes_,
                 expert_flop=expert_flop, expert_bytes=expert_bytes_,
-                gu_flop=gu_flop, gu_bytes=gu_bytes, gu_unit_bytes=2 * d * F * wb + gu_scales)
+                gu_flop=gu_flop, gu_bytes=gu_bytes, gu_unit_bytes=int(2 * d * F * wb + gu_scales))
 
 
 class HipEvents:
@@ -508,7 +514,8 @@ def main() -> None:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wl.act if wl.weight != "fp8" else "bf16 (fp8-e4m3 weights)",
+        "dtype": {"fp8": "bf16 (fp8-e4m3 weights)", "mxfp4": "bf16 (mxfp4 weights)"}.get(
+            wl.weight, wl.act),
         "data": "synthetic (seeded; random-init weights of the workload's shape)",
         "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "E": wl.E, "k": wl.k, "F": wl.F,
                    "local_experts": f"{wl.expert_begin}-{wl.expert_begin + wl.num_local - 1}",

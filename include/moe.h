@@ -43,18 +43,27 @@
  *  - A slot is s = t*k + i (token t, its i-th chosen expert).  Expert ids in
  *    index arrays are global ids in [0, E).
  *  - Formats: activations and the router matrix are MOE_F32 or MOE_BF16;
- *    expert weights are MOE_F32, MOE_BF16, or MOE_FP8_E4M3 (OCP E4M3FN codes,
+ *    expert weights are MOE_F32, MOE_BF16, MOE_FP8_E4M3 (OCP E4M3FN codes,
  *    one byte each) with float32 scales per 128x128 block of the stored
- *    matrix.  Supported (act, weight) pairs: (F32, F32), (BF16, BF16),
- *    (BF16, FP8_E4M3).  Accumulation is float32; intermediate h is rounded
- *    to the activation format.  FP8 block scales are finite, and each is 0
- *    (the block contributes nothing) or between 2^-100 and 2^100 in
- *    magnitude: the GEMMs fold them in by rescaling a float32 accumulator
- *    from one 128-deep K block to the next.
+ *    matrix, or MOE_MXFP4 (OCP MX FP4: E2M1 codes, two per byte along the
+ *    "in" dimension, element 2j in the low nibble of byte j, with one E8M0
+ *    scale byte 2^(s-127) per 32 consecutive "in" values).  Supported
+ *    (act, weight) pairs: (F32, F32), (BF16, BF16), (BF16, FP8_E4M3),
+ *    (BF16, MXFP4).  Accumulation is float32; intermediate h is rounded to
+ *    the activation format.  FP8 block scales are finite, and each is 0 (the
+ *    block contributes nothing) or between 2^-100 and 2^100 in magnitude:
+ *    the GEMMs fold them in by rescaling a float32 accumulator from one
+ *    128-deep K block to the next.  MXFP4 weights are widened exactly to
+ *    bfloat16 with their scale applied, which holds for scale bytes 0..252
+ *    (2^-127 .. 2^125); bytes 253..255 are outside the contract.
  *  - Expert weights are stored "out x in" (the math matrices transposed):
  *      w_gate, w_up : [E_l][F][d]      w_down : [E_l][d][F]
- *      s_gate, s_up : [E_l][F/128][d/128]   s_down : [E_l][d/128][F/128]
- *    so that Wg_e[c][f] = w_gate[e - expert_begin][f][c] (times its scale).
+ *    (MXFP4: [E_l][F][d/2] and [E_l][d][F/2] bytes), with scales
+ *      FP8:   s_gate, s_up : [E_l][F/128][d/128]   s_down : [E_l][d/128][F/128]  float32
+ *      MXFP4: s_gate, s_up : [E_l][d/32][F]        s_down : [E_l][F/32][d]       uint8 E8M0
+ *    (MXFP4 scales are stored K-block-major: the scales of one 32-value block
+ *    of all rows are contiguous), so that Wg_e[c][f] =
+ *    w_gate[e - expert_begin][f][c] times its scale.
  *
  * Errors: every call checks its arguments on the host before enqueuing
  * anything and returns MOE_ERR_INVALID_ARGUMENT (null required pointer, a
@@ -88,7 +97,7 @@ typedef enum {
   MOE_ERR_HIP = 4
 } moe_status_t;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype_t;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_MXFP4 = 3 } moe_dtype_t;
 
 /* Which call a workspace is sized for. */
 typedef enum {
@@ -158,14 +167,15 @@ moe_status_t moe_permute(const moe_problem_t* p, const int32_t* topk_idx, int32_
  *  x           [T][d] act format.
  *  sorted_slot [T*k], offsets [E_l + 1]: as produced by moe_permute.
  *  w_gate, w_up [E_l][F][d], w_down [E_l][d][F] in the weight format.
- *  s_gate, s_up, s_down: block scales (required for FP8_E4M3, else ignored).
+ *  s_gate, s_up, s_down: block scales (required for FP8_E4M3 and MXFP4, in
+ *              the layouts above; else ignored).
  *  topk_w      [T*k] float32 gates or NULL (y left unweighted).
  *  y           [T*k][d] act format output; rows >= N are not written.
  *  ws / ws_bytes: scratch of at least moe_workspace_size(p, MOE_CALL_EXPERT_FFN). */
 moe_status_t moe_expert_ffn(const moe_problem_t* p, const void* x, const int32_t* sorted_slot,
                             const int32_t* offsets, const void* w_gate, const void* w_up,
-                            const void* w_down, const float* s_gate, const float* s_up,
-                            const float* s_down, const float* topk_w, void* y, void* ws,
+                            const void* w_down, const void* s_gate, const void* s_up,
+                            const void* s_down, const float* topk_w, void* y, void* ws,
                             size_t ws_bytes, void* stream);
 
 /* Combine ("Mechanics of Token Routing": the output travels back), without
@@ -179,7 +189,7 @@ moe_status_t moe_combine(const moe_problem_t* p, const void* y, const int32_t* s
                          const float* topk_w, void* out, void* stream);
 
 /* Arguments of moe_forward.  Required: x, w_gate, w_up, w_down, out, and
- * either w_router, or logits as an input.  s_* are required for FP8 weights.
+ * either w_router, or logits as an input.  s_* are required for FP8 and MXFP4 weights.
  * The remaining outputs are optional (NULL = not wanted) and hold what the
  * individual calls above would write. */
 typedef struct {
@@ -189,9 +199,9 @@ typedef struct {
   const void* w_gate;       /* [E_l][F][d] weight format */
   const void* w_up;         /* [E_l][F][d] */
   const void* w_down;       /* [E_l][d][F] */
-  const float* s_gate;      /* FP8 block scales, see above */
-  const float* s_up;
-  const float* s_down;
+  const void* s_gate;       /* FP8 / MXFP4 block scales, see above */
+  const void* s_up;
+  const void* s_down;
   void* out;                /* [T][d] act output */
   float* logits;            /* [T][E] output (or input when w_router == NULL) */
   int32_t* topk_idx;        /* [T][k] */

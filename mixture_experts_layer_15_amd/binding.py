@@ -17,11 +17,11 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MOE_MI355X_LIB", os.path.join(PKG, "libmoe_mi355x.so"))
 
 MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
-MOE_F32, MOE_BF16, MOE_FP8_E4M3 = range(3)
+MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4 = range(4)
 MOE_CALL_PERMUTE, MOE_CALL_EXPERT_FFN, MOE_CALL_FORWARD, MOE_CALL_ROUTE = range(4)
 MOE_FORWARD_EVENTS = 7
 
-FMT = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
+FMT = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3, "mxfp4": MOE_MXFP4}
 
 
 class MoEError(RuntimeError):

@@ -7,7 +7,8 @@
 // needs bigger batches than you think": at decode batch sizes each expert sees
 // a handful of tokens and the expert GEMM only streams its weights from HBM;
 // prefill gives each expert many rows.  Both regimes use the kernels below,
-// with a 32-row tile for the first and a 128-row tile for the second.
+// with 32- or 64-row tiles for the first and 128- or 256-row tiles for the
+// second.
 //
 //   gate/up:  h[p] = silu(A_p Wg_j) * (A_p Wu_j),  A_p = x[sorted_slot[p] / k]
 //   down:     y[p] = (h[p] Wd_j) * gate(p)
@@ -25,6 +26,10 @@
 //  * FP8 weights: raw codes through LDS, widened exactly to bf16 at use, and
 //    a float32 scale per 128x128 block folded in by rescaling the accumulator
 //    at each 128-deep K block, so the weights enter MFMA unrounded;
+//  * MXFP4 weights ("Serving MoE models with expert parallelism on 8xH200",
+//    sections "Memory math for 8xH200" and "Quantization choices"): E2M1
+//    codes and their E8M0 block scales through LDS, each lane's 32 codes of a
+//    stage widened to bf16 with the scale applied in one exact conversion;
 //  * epilogues: silu(gate) * up rounded to bf16 (gate/up), or the product
 //    times the token's gate (down).
 #include <stdlib.h>
@@ -65,8 +70,8 @@ struct GemmArgs {
   int k;                       // top-k (slot -> token)
   const void* W0;              // gate (gate/up) or down weights
   const void* W1;              // up weights (gate/up)
-  const float* S0;             // FP8 scales for W0
-  const float* S1;             // FP8 scales for W1
+  const void* S0;              // scales for W0: FP8 float32 128x128 blocks, MXFP4 E8M0 bytes
+  const void* S1;              // scales for W1
   const float* topk_w;         // down epilogue gates, or null
   uint16_t* out;               // gate/up: h [S][Nout]; down: y [S][Nout]
   float* out_f32;              // router: logits without bias [rows][Nout]
@@ -171,6 +176,21 @@ __device__ __forceinline__ void lds_dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t
 #endif
 }
 
+// One 4-byte buffer -> LDS load per active lane (buffer_load_dword ... lds):
+// lane i's 4 bytes, from voffset + soffset in the buffer, land at lds + 4 i.
+__device__ __forceinline__ void lds_dma4_buf(__amdgpu_buffer_rsrc_t r, uint32_t voffset,
+                                             uint32_t soffset, unsigned char* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4,
+                                           voffset, soffset, 0, 0);
+#else
+  (void)r;
+  (void)voffset;
+  (void)soffset;
+  (void)lds;
+#endif
+}
+
 // One 4-byte global -> LDS load per active lane (global_load_lds_dword): lane
 // i's value lands at lds + 4 i.
 __device__ __forceinline__ void lds_dma4(const void* src, unsigned char* lds) {
@@ -182,22 +202,30 @@ __device__ __forceinline__ void lds_dma4(const void* src, unsigned char* lds) {
 #endif
 }
 
-template <int MB, int WM, int NB, int WN, bool kGateUp, bool kFP8, int kBK, int kStages>
+// kWBits: weight bits, 16 (bf16), 8 (FP8 E4M3) or 4 (MXFP4 E2M1)
+template <int MB, int WM, int NB, int WN, bool kGateUp, int kWBits, int kBK, int kStages>
 struct Cfg {
+  static constexpr bool kFP8 = kWBits == 8;
+  static constexpr bool kFP4 = kWBits == 4;
   static constexpr int kWaves = WM * WN;
   static constexpr int kThreads = kWave * kWaves;
   static constexpr int BM = 32 * MB * WM;    // tile rows
   static constexpr int BNW = 32 * NB * WN;   // weight rows per tile
   static constexpr int kRowA = kBK * 2;      // bytes per A row per stage
-  static constexpr int kRowB = kBK * (kFP8 ? 1 : 2);
+  static constexpr int kRowB = kBK * kWBits / 8;
   static constexpr int kChunksA = kRowA / 16;
   static constexpr int kChunksB = kRowB / 16;
   static constexpr int kStageA = BM * kRowA;
   static constexpr int kStageB = BNW * kRowB;
-  static constexpr int kStage = kStageA + kStageB;
+  // MXFP4: the stage's E8M0 scales after its weights, [kBK / 32][BNW] bytes
+  // (tile rows in feature order: gate/up: gate features, then up features)
+  static constexpr int kStageS = kFP4 ? (kBK / 32) * BNW : 0;
+  static constexpr int kStage = kStageA + kStageB + kStageS;
   static constexpr int kLoadsA = kStageA / (1024 * kWaves);  // 1 KB LDS-DMA loads per wave
   static constexpr int kLoadsB = kStageB / (1024 * kWaves);
-  static constexpr int kLoads = kLoadsA + kLoadsB;
+  static constexpr int kLoadsS = kFP4 ? 1 : 0;                // one 4-byte LDS-DMA per wave
+  static constexpr int kScaleLanes = kFP4 ? kStageS / (4 * kWaves) : 1;  // its active lanes
+  static constexpr int kLoads = kLoadsA + kLoadsB + kLoadsS;
   static constexpr int kSteps = kBK / 16;                     // MFMA K steps per stage
   static constexpr int kScaleSets = kFP8 ? BNW / 128 : 0;  // 128-row weight blocks per tile
   static constexpr int kMaxKBlocks = 65536 / 128;
@@ -211,16 +239,25 @@ struct Cfg {
   static_assert(!kFP8 || (kGateUp ? (BNW / 2) % 128 == 0 : BNW % 128 == 0),
                 "FP8 scales: whole 128-row weight blocks per tile (per half for gate/up)");
   static_assert(!kFP8 || kBK == 64, "FP8 raw codes are double-buffered per step pair");
+  static_assert(!kFP4 || kBK == 64, "MXFP4: one 16-byte chunk (two 32-value scale blocks) per lane per stage");
+  static_assert(!kFP4 || (kScaleLanes >= 1 && kScaleLanes <= kWave &&
+                          kStageS == 4 * kScaleLanes * kWaves),
+                "MXFP4 scales: one dword LDS-DMA per wave covers the stage's scales");
+  static_assert(!kFP4 || (kGateUp ? (BNW / 2) : BNW) % (4 * kScaleLanes) == 0,
+                "MXFP4 scales: a wave's dwords lie in one K block and one weight matrix");
   static_assert(kSteps % 2 == 0, "fragment buffers alternate by step");
 };
 
 // kRouter: the router products x W_r as one segment of `rows` token rows,
 // A = x read row by row, W0 = the router matrix stored [E][d], float32 output.
-template <int MB, int WM, int NB, int WN, bool kGateUp, bool kFP8, int kBK, int kStages,
+template <int MB, int WM, int NB, int WN, bool kGateUp, int kWBits, int kBK, int kStages,
           int kMinBlocks, bool kRouter>
 __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel(GemmArgs a) {
-  using C = Cfg<MB, WM, NB, WN, kGateUp, kFP8, kBK, kStages>;
-  static_assert(!kRouter || (!kGateUp && !kFP8), "router mode: plain bf16 GEMM");
+  using C = Cfg<MB, WM, NB, WN, kGateUp, kWBits, kBK, kStages>;
+  constexpr bool kFP8 = C::kFP8;
+  constexpr bool kFP4 = C::kFP4;
+  static_assert(kWBits == 16 || kFP8 || kFP4, "weight bits");
+  static_assert(!kRouter || (!kGateUp && kWBits == 16), "router mode: plain bf16 GEMM");
   constexpr int BNW = C::BNW;
   constexpr int H = NB / 2;  // gate/up: column blocks per half
   extern __shared__ __align__(16) unsigned char smem[];
@@ -234,7 +271,6 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
   const int g = l >> 5;  // which 8 of an MFMA step's 16 K values this lane holds
   const int wm = wave % WM;
   const int wn = wave / WM;
-  const int welem = kFP8 ? 1 : 2;  // bytes per weight element
   const int nK = a.K / kBK;
   const int KB = a.K / 128;
   const int n_sc = C::kScaleSets * KB;  // scale floats per item
@@ -312,7 +348,7 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
         // then up blocks)
         const int sb = o / KB, kb = o % KB;
         constexpr int kHalf = kGateUp ? C::kScaleSets / 2 : C::kScaleSets;
-        const float* S = (kGateUp && sb >= kHalf) ? a.S1 : a.S0;
+        const float* S = static_cast<const float*>((kGateUp && sb >= kHalf) ? a.S1 : a.S0);
         const int nblk = min(n0 / 128 + sb % kHalf, a.Nout / 128 - 1);
         lds_dma4(S + ((long long)j * (a.Nout / 128) + nblk) * KB + kb,
                  reinterpret_cast<unsigned char*>(sc_lds + buf * n_sc + c0));
@@ -327,6 +363,8 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
   __amdgpu_buffer_rsrc_t rsA, rsB0, rsB1;  // A rows; gate or down weights; up weights
   uint32_t offA[C::kLoadsA];
   uint32_t offB[C::kLoadsB];
+  __amdgpu_buffer_rsrc_t rsS;  // MXFP4: the scale matrix this wave's scale loads read
+  uint32_t offS = 0;
   // weight instruction i of this wave reads up rows (one half of the tile)
   auto b_up = [&](int i) -> bool {
     return kGateUp && ((wave * C::kLoadsB + i) * kWave) / C::kChunksB >= BNW / 2;
@@ -349,7 +387,8 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
                                     : (uint32_t)min(r, row_end - 1 - row0);
       offA[i] = arow * arow_bytes + c * 16;
     }
-    const uint32_t wmat = (uint32_t)a.Nout * a.K * welem;  // bytes of one expert's matrix
+    const uint32_t wrow_bytes = (uint32_t)a.K * kWBits / 8;
+    const uint32_t wmat = (uint32_t)a.Nout * wrow_bytes;  // bytes of one expert's matrix
     rsB0 = buffer_rsrc(static_cast<const unsigned char*>(a.W0) + (size_t)j * wmat, wmat);
     rsB1 = kGateUp ? buffer_rsrc(static_cast<const unsigned char*>(a.W1) + (size_t)j * wmat, wmat)
                    : rsB0;
@@ -360,7 +399,20 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
       const int c = (P % C::kChunksB) ^ ((r / (256 / C::kRowB)) % C::kChunksB);
       const int rr = (kGateUp && r >= BNW / 2) ? r - BNW / 2 : r;
       const uint32_t wrow = (uint32_t)min(n0 + feat_of_row(rr), a.Nout - 1);
-      offB[i] = wrow * (uint32_t)(a.K * welem) + c * 16;
+      offB[i] = wrow * wrow_bytes + c * 16;
+    }
+    if constexpr (kFP4) {
+      // this wave's dword of a stage's scale block: K block kb of the stage,
+      // tile bytes [wb % BNW, + 4 kScaleLanes) (wave-uniform matrix and K
+      // block); lane l: features fo .. fo + 3 of that matrix
+      const uint32_t smat = (uint32_t)(a.K / 32) * a.Nout;  // bytes of one expert's scales
+      const int wb = wave * C::kScaleLanes * 4;
+      const int kb = wb / BNW;
+      const bool up = kGateUp && (wb % BNW) >= BNW / 2;
+      const int fo = (wb % BNW) - (up ? BNW / 2 : 0) + 4 * l;
+      rsS = buffer_rsrc(static_cast<const unsigned char*>(up ? a.S1 : a.S0) + (size_t)j * smat,
+                        smat);
+      offS = (uint32_t)kb * a.Nout + (uint32_t)min(n0 + fo, a.Nout - 4);
     }
   };
 
@@ -372,8 +424,13 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
         lds_dma16_buf(rsA, offA[i], (uint32_t)(Q) * kBK * 2,                                    \
                       sb_ + (wave * C::kLoadsA + i) * 1024);                                    \
     _Pragma("unroll") for (int i = 0; i < C::kLoadsB; ++i)                                      \
-        lds_dma16_buf(b_up(i) ? rsB1 : rsB0, offB[i], (uint32_t)(Q) * kBK * welem,              \
+        lds_dma16_buf(b_up(i) ? rsB1 : rsB0, offB[i], (uint32_t)(Q) * C::kRowB,                \
                       sb_ + C::kStageA + (wave * C::kLoadsB + i) * 1024);                       \
+    if constexpr (kFP4) {                                                                       \
+      if (l < C::kScaleLanes)                                                                   \
+        lds_dma4_buf(rsS, offS, (uint32_t)(Q) * (kBK / 32) * a.Nout,                            \
+                     sb_ + C::kStageA + C::kStageB + wave * C::kScaleLanes * 4);               \
+    }                                                                                           \
   } while (0)
 
   int item = it_begin + slot;
@@ -409,17 +466,38 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
   // step s; an FP8 lane holds one 16-byte chunk (16 K values) for steps
   // 2p and 2p + 1.
   bf16x8_t af[2][MB];
-  bf16x8_t bf[2][kFP8 ? 1 : NB];
+  bf16x8_t bf[2][(kFP8 || kFP4) ? 1 : NB];
   u32x4_t raw8[2][kFP8 ? NB : 1];
+  // MXFP4: one 16-byte chunk (32 codes: K values 32 g .. 32 g + 31 of the
+  // stage) and its block scale per weight block, by stage parity; step s
+  // uses codes 8 s .. 8 s + 7
+  u32x4_t raw4[2][kFP4 ? NB : 1];
+  float sc4[2][kFP4 ? NB : 1];
+  // MXFP4: byte of this lane's weight row in a stage's scale block (feature
+  // order inside the tile)
+  auto srow = [&](int n) -> int {
+    if (kGateUp) return (n < H ? 0 : BNW / 2) + feat_of_row(wn * H * 32 + (n % H) * 32 + (l & 31));
+    return feat_of_row(wn * NB * 32 + n * 32 + (l & 31));
+  };
   auto read_frags = [&](int stage, int s, int buf) {
     const unsigned char* As = smem + (stage % kStages) * C::kStage;
     const unsigned char* Bs = As + C::kStageA;
-    const int cA = kFP8 ? (4 * (s >> 1) + 2 * g + (s & 1)) : (2 * s + g);
+    const int cA = kFP4 ? (4 * g + s) : kFP8 ? (4 * (s >> 1) + 2 * g + (s & 1)) : (2 * s + g);
 #pragma unroll
     for (int m = 0; m < MB; ++m)
       af[buf][m] = *reinterpret_cast<const bf16x8_t*>(
           As + lds_off<C::kRowA>(arow_base + m * 32, cA));
-    if constexpr (kFP8) {
+    if constexpr (kFP4) {
+      if (s == 0) {
+        const unsigned char* Ss = Bs + C::kStageB;
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+          raw4[stage & 1][n] = *reinterpret_cast<const u32x4_t*>(
+              Bs + lds_off<C::kRowB>(brow(n), g));
+          sc4[stage & 1][n] = e8m0_to_f32(Ss[g * BNW + srow(n)]);
+        }
+      }
+    } else if constexpr (kFP8) {
       if ((s & 1) == 0) {
 #pragma unroll
         for (int n = 0; n < NB; ++n)
@@ -499,11 +577,14 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
       for (int n = 0; n < NB; ++n) rsc[n] = 1.0f, zblk[n] = false;
     }
 
-    auto mfma_step = [&](int s, int buf) {
+    // sp: parity of the pipeline stage (MXFP4 fragments are kept per stage)
+    auto mfma_step = [&](int s, int buf, int sp) {
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
         bf16x8_t bfr;
-        if constexpr (kFP8) {
+        if constexpr (kFP4) {
+          bfr = e2m1x8_to_bf16x8(raw4[sp][n][s], sc4[sp][n]);
+        } else if constexpr (kFP8) {
           u32x4_t r = raw8[(s >> 1) & 1][n];
           if (anyz && zblk[n]) r = u32x4_t{0u, 0u, 0u, 0u};
           const u32x2_t lo = e4m3x4_to_bf16x4(r[(s & 1) * 2]);
@@ -552,13 +633,13 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
       for (int s = 0; s < C::kSteps; ++s) {
         if (s + 1 < C::kSteps) {
           read_frags(base + ks, s + 1, (s + 1) & 1);
-          mfma_step(s, s & 1);
+          mfma_step(s, s & 1, (base + ks) & 1);
           // alternate MFMA and LDS read (the next step's fragments): bursts of
           // reads stall the issuing waves, alternating keeps the matrix pipe fed
           if (kFP8 && (s + 1) % 2 != 0)  // FP8 weights are read every other step
             sched_alternate<MB, MB * NB>();
           else
-            sched_alternate<MB + NB, MB * NB>();
+            sched_alternate<MB + (kFP4 ? 0 : NB), MB * NB>();
         } else {
           const bool more = ks + 1 < nK;
           __builtin_amdgcn_sched_barrier(0);
@@ -573,8 +654,8 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
           if (ks + kStages < nK) MOE_ISSUE_STAGE(ks + kStages, base + ks + kStages);
           __builtin_amdgcn_sched_barrier(0);
           if (more) read_frags(base + ks + 1, 0, 0);
-          mfma_step(s, s & 1);
-          if (more) sched_alternate<MB + NB, MB * NB>();
+          mfma_step(s, s & 1, (base + ks) & 1);
+          if (more) sched_alternate<MB + (kFP4 ? 2 * NB : NB), MB * NB>();
         }
       }
     }
@@ -736,11 +817,11 @@ int num_cu() {
   return g_num_cu;
 }
 
-template <int MB, int WM, int NB, int WN, bool kGateUp, bool kFP8, int kBK, int kStages,
+template <int MB, int WM, int NB, int WN, bool kGateUp, int kWBits, int kBK, int kStages,
           int kMinBlocks, bool kRouter = false>
 hipError_t launch_gemm(const GemmArgs& a, long long max_items, hipStream_t st) {
-  using C = Cfg<MB, WM, NB, WN, kGateUp, kFP8, kBK, kStages>;
-  auto kern = grouped_gemm_kernel<MB, WM, NB, WN, kGateUp, kFP8, kBK, kStages, kMinBlocks, kRouter>;
+  using C = Cfg<MB, WM, NB, WN, kGateUp, kWBits, kBK, kStages>;
+  auto kern = grouped_gemm_kernel<MB, WM, NB, WN, kGateUp, kWBits, kBK, kStages, kMinBlocks, kRouter>;
   static bool attr = false;
   if (!attr) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -755,7 +836,7 @@ hipError_t launch_gemm(const GemmArgs& a, long long max_items, hipStream_t st) {
   grid = (grid + kNumXcd - 1) / kNumXcd * kNumXcd;
   if (grid < kNumXcd) grid = kNumXcd;
   // stages, then the FP8 scales of two items
-  const size_t lds = (size_t)kStages * C::kStage + (kFP8 ? 2u * C::kScaleSets * (a.K / 128) * 4 : 0);
+  const size_t lds = (size_t)kStages * C::kStage + (C::kFP8 ? 2u * C::kScaleSets * (a.K / 128) * 4 : 0);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::kThreads), lds, st, a);
   return hipGetLastError();
 }
@@ -768,11 +849,13 @@ hipError_t launch_gemm(const GemmArgs& a, long long max_items, hipStream_t st) {
 // experts hold a few hundred rows (less M padding) or 256 x 256 when they hold
 // a thousand or more (fewer bytes staged per MFMA).  FP8 weights: eight waves
 // of 64 x 128 in 128 x 512 tiles, 64-deep K steps (one byte per code) and 3
-// stages.
-enum class Plan { kF32, kDecode, kDecode64, kWide, kBig, kFp8 };
+// stages.  MXFP4 weights: the 32 x 256 decode tile with 8 stages (a stage
+// holds a quarter of the bf16 weight bytes), else the FP8 tile shape with 4.
+enum class Plan { kF32, kDecode, kDecode64, kWide, kBig, kFp8, kDecodeFp4, kFp4 };
 
 Plan plan_of(const Shape& s) {
   if (s.weight == kF32) return Plan::kF32;
+  if (s.weight == kFP4) return s.S <= 64LL * s.El ? Plan::kDecodeFp4 : Plan::kFp4;
   if (s.S <= 16LL * s.El) return Plan::kDecode;
   if (s.S <= 64LL * s.El) return s.weight == kFP8 ? Plan::kDecode : Plan::kDecode64;
   if (s.weight == kFP8) return Plan::kFp8;
@@ -780,13 +863,15 @@ Plan plan_of(const Shape& s) {
 }
 
 bool use_decode_tiles(const Shape& s) {
-  return plan_of(s) == Plan::kDecode || plan_of(s) == Plan::kDecode64;
+  const Plan p = plan_of(s);
+  return p == Plan::kDecode || p == Plan::kDecode64 || p == Plan::kDecodeFp4;
 }
 
 int tile_bm(const Shape& s) {
   switch (plan_of(s)) {
     case Plan::kF32: return kF32BM;
     case Plan::kDecode: return 32;
+    case Plan::kDecodeFp4: return 32;
     case Plan::kDecode64: return 64;
     case Plan::kBig: return 256;
     default: return 128;
@@ -815,9 +900,9 @@ hipError_t router_gemm(const Shape& s, const void* x, const void* w_router_t, fl
   // 32 x 256 tiles (four waves side by side along the experts); 64-row tiles
   // once there are enough of them, which halves the router matrix re-reads
   if (s.T >= 16384)
-    return launch_gemm<2, 1, 2, 4, false, false, 64, 4, 1, true>(
+    return launch_gemm<2, 1, 2, 4, false, 16, 64, 4, 1, true>(
         a, (long long)((s.T + 63) / 64) * a.n_tiles_n, st);
-  return launch_gemm<1, 1, 2, 4, false, false, 64, 4, 1, true>(
+  return launch_gemm<1, 1, 2, 4, false, 16, 64, 4, 1, true>(
       a, (long long)((s.T + 31) / 32) * a.n_tiles_n, st);
 }
 
@@ -838,8 +923,8 @@ size_t ffn_ws_bytes(const Shape& s) {
 
 hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
                       const int32_t* offsets, const void* w_gate, const void* w_up,
-                      const void* w_down, const float* s_gate, const float* s_up,
-                      const float* s_down, const float* topk_w, void* y, void* ws,
+                      const void* w_down, const void* s_gate, const void* s_up,
+                      const void* s_down, const float* topk_w, void* y, void* ws,
                       hipStream_t st, bool schedule_ready, hipEvent_t const* ev) {
   if (s.S == 0) return hipSuccess;
   const FfnSchedule sv = ffn_schedule_view(s, ws);
@@ -911,42 +996,58 @@ hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
       gu.n_tiles_n = ntn(s.F, 128);
       dn.n_tiles_n = ntn(s.d, 256);
       if (fp8) {
-        e = launch_gemm<1, 1, 2, 4, true, true, 64, 4, 2>(gu, mt * gu.n_tiles_n, st);
+        e = launch_gemm<1, 1, 2, 4, true, 8, 64, 4, 2>(gu, mt * gu.n_tiles_n, st);
         if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-        if (e == hipSuccess) e = launch_gemm<1, 1, 2, 4, false, true, 64, 4, 2>(dn, mt * dn.n_tiles_n, st);
+        if (e == hipSuccess) e = launch_gemm<1, 1, 2, 4, false, 8, 64, 4, 2>(dn, mt * dn.n_tiles_n, st);
       } else {
-        e = launch_gemm<1, 1, 2, 4, true, false, 64, 4, 1>(gu, mt * gu.n_tiles_n, st);
+        e = launch_gemm<1, 1, 2, 4, true, 16, 64, 4, 1>(gu, mt * gu.n_tiles_n, st);
         if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-        if (e == hipSuccess) e = launch_gemm<1, 1, 2, 4, false, false, 64, 4, 1>(dn, mt * dn.n_tiles_n, st);
+        if (e == hipSuccess) e = launch_gemm<1, 1, 2, 4, false, 16, 64, 4, 1>(dn, mt * dn.n_tiles_n, st);
       }
       break;
     case Plan::kDecode64:
       gu.n_tiles_n = ntn(s.F, 128);
       dn.n_tiles_n = ntn(s.d, 256);
-      e = launch_gemm<2, 1, 2, 4, true, false, 64, 4, 1>(gu, mt * gu.n_tiles_n, st);
+      e = launch_gemm<2, 1, 2, 4, true, 16, 64, 4, 1>(gu, mt * gu.n_tiles_n, st);
       if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-      if (e == hipSuccess) e = launch_gemm<2, 1, 2, 4, false, false, 64, 4, 1>(dn, mt * dn.n_tiles_n, st);
+      if (e == hipSuccess) e = launch_gemm<2, 1, 2, 4, false, 16, 64, 4, 1>(dn, mt * dn.n_tiles_n, st);
       break;
     case Plan::kFp8:
       gu.n_tiles_n = ntn(s.F, 256);
       dn.n_tiles_n = ntn(s.d, 512);
-      e = launch_gemm<2, 2, 4, 4, true, true, 64, 3, 1>(gu, mt * gu.n_tiles_n, st);
+      e = launch_gemm<2, 2, 4, 4, true, 8, 64, 3, 1>(gu, mt * gu.n_tiles_n, st);
       if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-      if (e == hipSuccess) e = launch_gemm<2, 2, 4, 4, false, true, 64, 3, 1>(dn, mt * dn.n_tiles_n, st);
+      if (e == hipSuccess) e = launch_gemm<2, 2, 4, 4, false, 8, 64, 3, 1>(dn, mt * dn.n_tiles_n, st);
       break;
     case Plan::kWide:
       gu.n_tiles_n = ntn(s.F, 256);
       dn.n_tiles_n = ntn(s.d, 512);
-      e = launch_gemm<2, 2, 4, 4, true, false, 32, 4, 1>(gu, mt * gu.n_tiles_n, st);
+      e = launch_gemm<2, 2, 4, 4, true, 16, 32, 4, 1>(gu, mt * gu.n_tiles_n, st);
       if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-      if (e == hipSuccess) e = launch_gemm<2, 2, 4, 4, false, false, 32, 4, 1>(dn, mt * dn.n_tiles_n, st);
+      if (e == hipSuccess) e = launch_gemm<2, 2, 4, 4, false, 16, 32, 4, 1>(dn, mt * dn.n_tiles_n, st);
       break;
     case Plan::kBig:
       gu.n_tiles_n = ntn(s.F, 128);
       dn.n_tiles_n = ntn(s.d, 256);
-      e = launch_gemm<2, 4, 4, 2, true, false, 32, 4, 1>(gu, mt * gu.n_tiles_n, st);
+      e = launch_gemm<2, 4, 4, 2, true, 16, 32, 4, 1>(gu, mt * gu.n_tiles_n, st);
       if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-      if (e == hipSuccess) e = launch_gemm<2, 4, 4, 2, false, false, 32, 4, 1>(dn, mt * dn.n_tiles_n, st);
+      if (e == hipSuccess) e = launch_gemm<2, 4, 4, 2, false, 16, 32, 4, 1>(dn, mt * dn.n_tiles_n, st);
+      break;
+    case Plan::kDecodeFp4:
+      // 4-bit weights: a 32 x 256 tile streams a quarter of the bf16 bytes
+      // per stage, so eight stages keep as many bytes in flight
+      gu.n_tiles_n = ntn(s.F, 128);
+      dn.n_tiles_n = ntn(s.d, 256);
+      e = launch_gemm<1, 1, 2, 4, true, 4, 64, 8, 1>(gu, mt * gu.n_tiles_n, st);
+      if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
+      if (e == hipSuccess) e = launch_gemm<1, 1, 2, 4, false, 4, 64, 8, 1>(dn, mt * dn.n_tiles_n, st);
+      break;
+    case Plan::kFp4:
+      gu.n_tiles_n = ntn(s.F, 256);
+      dn.n_tiles_n = ntn(s.d, 512);
+      e = launch_gemm<2, 2, 4, 4, true, 4, 64, 4, 1>(gu, mt * gu.n_tiles_n, st);
+      if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
+      if (e == hipSuccess) e = launch_gemm<2, 2, 4, 4, false, 4, 64, 4, 1>(dn, mt * dn.n_tiles_n, st);
       break;
     case Plan::kF32:
       break;

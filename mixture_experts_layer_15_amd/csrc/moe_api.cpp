@@ -13,7 +13,7 @@ using moe::Shape;
 
 bool supported_pair(int act, int weight) {
   return (act == MOE_F32 && weight == MOE_F32) || (act == MOE_BF16 && weight == MOE_BF16) ||
-         (act == MOE_BF16 && weight == MOE_FP8_E4M3);
+         (act == MOE_BF16 && weight == MOE_FP8_E4M3) || (act == MOE_BF16 && weight == MOE_MXFP4);
 }
 
 // Shape checks shared by every call.  Returns MOE_OK and fills `s` on success.
@@ -24,8 +24,7 @@ moe_status_t check_problem(const moe_problem_t* p, Shape* s) {
   if (p->expert_begin < 0 || p->num_local < 1) return MOE_ERR_INVALID_ARGUMENT;
   if ((long long)p->expert_begin + p->num_local > p->E) return MOE_ERR_INVALID_ARGUMENT;
   if (p->d % 128 != 0 || p->F % 128 != 0) return MOE_ERR_INVALID_ARGUMENT;
-  if (p->act < MOE_F32 || p->act > MOE_FP8_E4M3 || p->weight < MOE_F32 ||
-      p->weight > MOE_FP8_E4M3)
+  if (p->act < MOE_F32 || p->act > MOE_MXFP4 || p->weight < MOE_F32 || p->weight > MOE_MXFP4)
     return MOE_ERR_INVALID_ARGUMENT;
   if (!supported_pair(p->act, p->weight)) return MOE_ERR_UNSUPPORTED;
   if (p->E > moe::kMaxExperts || p->d > 65536 || p->F > 65536) return MOE_ERR_UNSUPPORTED;
@@ -34,8 +33,9 @@ moe_status_t check_problem(const moe_problem_t* p, Shape* s) {
   // the expert GEMMs address x and one expert's weight matrix with 32-bit
   // offsets
   const long long ab = p->act == MOE_F32 ? 4 : 2;
-  const long long wb = p->weight == MOE_F32 ? 4 : p->weight == MOE_BF16 ? 2 : 1;
-  if ((long long)p->T * p->d * ab >= (1LL << 32) || (long long)p->F * p->d * wb >= (1LL << 32))
+  const long long wbits = p->weight == MOE_F32 ? 32 : p->weight == MOE_BF16 ? 16
+                        : p->weight == MOE_FP8_E4M3 ? 8 : 4;
+  if ((long long)p->T * p->d * ab >= (1LL << 32) || (long long)p->F * p->d * wbits / 8 >= (1LL << 32))
     return MOE_ERR_UNSUPPORTED;
   s->T = p->T;
   s->d = p->d;
@@ -156,8 +156,8 @@ moe_status_t moe_permute(const moe_problem_t* p, const int32_t* topk_idx, int32_
 
 moe_status_t moe_expert_ffn(const moe_problem_t* p, const void* x, const int32_t* sorted_slot,
                             const int32_t* offsets, const void* w_gate, const void* w_up,
-                            const void* w_down, const float* s_gate, const float* s_up,
-                            const float* s_down, const float* topk_w, void* y, void* ws,
+                            const void* w_down, const void* s_gate, const void* s_up,
+                            const void* s_down, const float* topk_w, void* y, void* ws,
                             size_t ws_bytes, void* stream) {
   Shape s;
   moe_status_t st = check_problem(p, &s);
@@ -165,7 +165,8 @@ moe_status_t moe_expert_ffn(const moe_problem_t* p, const void* x, const int32_t
   if (x == nullptr || sorted_slot == nullptr || offsets == nullptr || w_gate == nullptr ||
       w_up == nullptr || w_down == nullptr || y == nullptr)
     return MOE_ERR_INVALID_ARGUMENT;
-  if (s.weight == MOE_FP8_E4M3 && (s_gate == nullptr || s_up == nullptr || s_down == nullptr))
+  if ((s.weight == MOE_FP8_E4M3 || s.weight == MOE_MXFP4) &&
+      (s_gate == nullptr || s_up == nullptr || s_down == nullptr))
     return MOE_ERR_INVALID_ARGUMENT;
   const size_t need = moe::ffn_ws_bytes(s);
   if (ws == nullptr || ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
@@ -193,7 +194,7 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_forward_args_t* a, vo
       a->w_down == nullptr || a->out == nullptr)
     return MOE_ERR_INVALID_ARGUMENT;
   if (a->w_router == nullptr && a->logits == nullptr) return MOE_ERR_INVALID_ARGUMENT;
-  if (s.weight == MOE_FP8_E4M3 &&
+  if ((s.weight == MOE_FP8_E4M3 || s.weight == MOE_MXFP4) &&
       (a->s_gate == nullptr || a->s_up == nullptr || a->s_down == nullptr))
     return MOE_ERR_INVALID_ARGUMENT;
   const ForwardLayout L = forward_layout(s);

@@ -39,6 +39,28 @@ __device__ __forceinline__ u32x2_t e4m3x4_to_bf16x4(uint32_t q) {
   return u32x2_t{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
+// One E8M0 scale byte -> its float32 value 2^(s - 127) (s = 0 is the
+// float32 subnormal 2^-127; s = 255, NaN in the format, is outside the
+// library's contract).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
+  return __uint_as_float(s ? (s << 23) : 0x00400000u);
+}
+
+// Eight OCP E2M1 codes (one dword, element 2j in the low nibble of byte j)
+// times a power-of-two scale -> eight bfloat16.  Exact: an E2M1 value has at
+// most 2 significant bits, so every product with a scale in 2^-127 .. 2^125
+// is a bfloat16 (v_cvt_scalef32_pk_bf16_fp4, one byte per instruction).
+__device__ __forceinline__ bf16x8_t e2m1x8_to_bf16x8(uint32_t q, float scale) {
+  const bf16x2_t b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, 0);
+  const bf16x2_t b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, 1);
+  const bf16x2_t b2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, 2);
+  const bf16x2_t b3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, 3);
+  return __builtin_bit_cast(bf16x8_t, u32x4_t{__builtin_bit_cast(uint32_t, b0),
+                                              __builtin_bit_cast(uint32_t, b1),
+                                              __builtin_bit_cast(uint32_t, b2),
+                                              __builtin_bit_cast(uint32_t, b3)});
+}
+
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 // Wave-wide sum with a fixed butterfly order (deterministic).

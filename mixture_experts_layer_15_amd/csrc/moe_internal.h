@@ -8,7 +8,7 @@
 
 namespace moe {
 
-enum Fmt : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
+enum Fmt : int { kF32 = 0, kBF16 = 1, kFP8 = 2, kFP4 = 3 };
 
 constexpr int kMaxExperts = 512;      // E limit (router top-k and permutation LDS tables)
 constexpr int kPermuteChunk = 2048;   // slots per workgroup in the permutation kernels
@@ -52,8 +52,8 @@ size_t ffn_ws_bytes(const Shape& s);
 // the gate/up GEMM and the down GEMM.
 hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
                       const int32_t* offsets, const void* w_gate, const void* w_up,
-                      const void* w_down, const float* s_gate, const float* s_up,
-                      const float* s_down, const float* topk_w, void* y, void* ws,
+                      const void* w_down, const void* s_gate, const void* s_up,
+                      const void* s_down, const float* topk_w, void* y, void* ws,
                       hipStream_t st, bool schedule_ready = false,
                       hipEvent_t const* stage_events = nullptr);
 

@@ -19,7 +19,12 @@ Draw order for a given seed (``numpy.random.default_rng``, PCG64): ``x``,
 (fan_in = d for router, gate and up; F for down) and then rounded to
 nearest-even into the storage format.  FP8 weights use per-128x128-block
 scales ``s = amax(block) / 448`` (``s = 1`` for an all-zero block) and codes
-``RNE(W / s)`` clamped to +-448.
+``RNE(W / s)`` clamped to +-448.  MXFP4 weights use, per 32 consecutive "in"
+values of a row, the shared exponent ``X = floor(log2(amax)) - 2`` (the OCP MX
+recipe: 2 is E2M1's largest exponent; ``X = 0`` for an all-zero block) stored
+as the E8M0 byte ``X + 127`` (clamped to 0..252), and codes = ``W / 2^X``
+rounded to the nearest E2M1 value (ties to the smaller magnitude), clamped
+to +-6.
 """
 from __future__ import annotations
 
@@ -32,6 +37,10 @@ import torch
 
 FP8_MAX = 448.0
 BLOCK = 128
+MX_BLOCK = 32
+# E2M1 magnitudes of codes 0..7 and the midpoints between neighbours
+_E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+_E2M1_MID = (_E2M1[1:] + _E2M1[:-1]) / 2
 
 
 @dataclasses.dataclass(frozen=True)
@@ -45,7 +54,7 @@ class Workload:
     expert_begin: int
     num_local: int
     act: str            # "f32" | "bf16"
-    weight: str         # "f32" | "bf16" | "fp8"
+    weight: str         # "f32" | "bf16" | "fp8" | "mxfp4"
     bias: tuple = ()    # () | ("zipf", s, scale) | ("gauss", sd)
     seed: int = 0
     regime: str = "prefill"   # "decode" (HBM-bound) | "prefill" (MFMA-bound) | "tiny"
@@ -67,6 +76,9 @@ WORKLOADS = {
     "mixtral": Workload("mixtral_8x7b_T4096_d4096_E8_k2_F14336_gauss1.0", T=4096, d=4096, E=8, k=2,
                         F=14336, expert_begin=0, num_local=8, act="bf16", weight="bf16",
                         bias=("gauss", 1.0), seed=4),
+    "decode_mxfp4": Workload("qwen3_30b_a3b_decode_T64_d2048_E128_k8_F768_mxfp4", T=64, d=2048,
+                             E=128, k=8, F=768, expert_begin=0, num_local=128, act="bf16",
+                             weight="mxfp4", seed=6, regime="decode"),
     "dsv3_rank": Workload("deepseek_v3_ep_rank_T16384_d7168_E256_local0-31_k8_F2048_fp8_zipf1.2",
                           T=16384, d=7168, E=256, k=8, F=2048, expert_begin=0, num_local=32,
                           act="bf16", weight="fp8", bias=("zipf", 1.2, 2.0), seed=5),
@@ -80,10 +92,12 @@ class Problem:
     x: torch.Tensor                   # [T, d] float32 | bfloat16
     w_router: torch.Tensor            # [d, E] same dtype as x
     bias: Optional[torch.Tensor]      # [E] float32 or None
-    w_gate: torch.Tensor              # [E_l, F, d] float32 | bfloat16 | uint8 (fp8 codes)
+    w_gate: torch.Tensor              # [E_l, F, d] float32 | bfloat16 | uint8 (fp8 codes);
+                                      # mxfp4: [E_l, F, d/2] uint8, two codes per byte
     w_up: torch.Tensor                # [E_l, F, d]
     w_down: torch.Tensor              # [E_l, d, F]
-    s_gate: Optional[torch.Tensor] = None   # [E_l, F/128, d/128] float32 (fp8 only)
+    s_gate: Optional[torch.Tensor] = None   # fp8: [E_l, F/128, d/128] float32;
+                                            # mxfp4: [E_l, d/32, F] uint8 E8M0
     s_up: Optional[torch.Tensor] = None
     s_down: Optional[torch.Tensor] = None   # [E_l, d/128, F/128]
 
@@ -115,6 +129,23 @@ def quantize_fp8_block128(w32: np.ndarray):
     return q.contiguous(), s.contiguous()
 
 
+def quantize_mxfp4(w32: np.ndarray):
+    """float32 [R, C] -> (uint8 codes [R, C/2], two per byte, element 2j in
+    the low nibble of byte j; uint8 E8M0 scales [C/32, R], block-major)."""
+    R, C = w32.shape
+    assert C % MX_BLOCK == 0
+    blocks = np.asarray(w32, dtype=np.float64).reshape(R, C // MX_BLOCK, MX_BLOCK)
+    amax = np.abs(blocks).max(axis=2)
+    with np.errstate(divide="ignore"):
+        X = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, 0.0)
+    sbyte = np.clip(X + 127, 0, 252).astype(np.int64)
+    v = blocks / np.exp2(sbyte - 127)[:, :, None]
+    mag = np.searchsorted(_E2M1_MID, np.abs(v), side="left")  # ties -> smaller magnitude
+    codes = (mag | np.where(v < 0, 8, 0)).astype(np.uint8).reshape(R, C)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return torch.from_numpy(packed), torch.from_numpy(np.ascontiguousarray(sbyte.T.astype(np.uint8)))
+
+
 def router_bias(wl: Workload, rng: np.random.Generator) -> Optional[np.ndarray]:
     """Per-expert logit bias that skews the expert load.
 
@@ -144,15 +175,20 @@ def make_problem(wl: Workload, seed: Optional[int] = None) -> Problem:
     bias = None if b is None else torch.from_numpy(b)
 
     wfmt = wl.weight
-    gdt = torch.uint8 if wfmt == "fp8" else _act_dtype(wfmt)
-    w_gate = torch.empty((El, F, d), dtype=gdt)
-    w_up = torch.empty((El, F, d), dtype=gdt)
-    w_down = torch.empty((El, d, F), dtype=gdt)
+    gdt = torch.uint8 if wfmt in ("fp8", "mxfp4") else _act_dtype(wfmt)
+    div = 2 if wfmt == "mxfp4" else 1   # two 4-bit codes per byte along "in"
+    w_gate = torch.empty((El, F, d // div), dtype=gdt)
+    w_up = torch.empty((El, F, d // div), dtype=gdt)
+    w_down = torch.empty((El, d, F // div), dtype=gdt)
     s_gate = s_up = s_down = None
     if wfmt == "fp8":
         s_gate = torch.empty((El, F // BLOCK, d // BLOCK), dtype=torch.float32)
         s_up = torch.empty_like(s_gate)
         s_down = torch.empty((El, d // BLOCK, F // BLOCK), dtype=torch.float32)
+    if wfmt == "mxfp4":
+        s_gate = torch.empty((El, d // MX_BLOCK, F), dtype=torch.uint8)
+        s_up = torch.empty_like(s_gate)
+        s_down = torch.empty((El, F // MX_BLOCK, d), dtype=torch.uint8)
     gd, gf = np.float32(1.0 / math.sqrt(d)), np.float32(1.0 / math.sqrt(F))
     for j in range(El):
         g = rng.standard_normal((F, d), dtype=np.float32) * gd
@@ -162,6 +198,10 @@ def make_problem(wl: Workload, seed: Optional[int] = None) -> Problem:
             w_gate[j], s_gate[j] = quantize_fp8_block128(g)
             w_up[j], s_up[j] = quantize_fp8_block128(u)
             w_down[j], s_down[j] = quantize_fp8_block128(dn)
+        elif wfmt == "mxfp4":
+            w_gate[j], s_gate[j] = quantize_mxfp4(g)
+            w_up[j], s_up[j] = quantize_mxfp4(u)
+            w_down[j], s_down[j] = quantize_mxfp4(dn)
         else:
             w_gate[j] = _store(g, wfmt)
             w_up[j] = _store(u, wfmt)

@@ -69,11 +69,21 @@ def test_invalid_shapes_rejected(lib, kw):
 
 
 @pytest.mark.parametrize("act,weight", [("f32", "bf16"), ("bf16", "f32"), ("f32", "fp8"),
-                                        ("fp8", "fp8"), ("fp8", "bf16")])
+                                        ("fp8", "fp8"), ("fp8", "bf16"), ("f32", "mxfp4"),
+                                        ("mxfp4", "mxfp4"), ("mxfp4", "bf16")])
 def test_unsupported_format_pairs(lib, act, weight):
     p = _p(act=act, weight=weight)
     st = lib.moe_combine(ctypes.byref(p), FAKE, FAKE, None, FAKE, None)
     assert st == B.MOE_ERR_UNSUPPORTED
+
+
+def test_mxfp4_needs_its_scales(lib):
+    p = _p(weight="mxfp4")
+    ws = B.moe_workspace_size(p, B.MOE_CALL_EXPERT_FFN)
+    assert ws > 0
+    st = lib.moe_expert_ffn(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                            None, FAKE, FAKE, ws, None)
+    assert st == B.MOE_ERR_INVALID_ARGUMENT
 
 
 def test_limits_are_unsupported_not_invalid(lib):

@@ -18,7 +18,8 @@ from oracle import moe_oracle as orc
 
 pytestmark = pytest.mark.gpu
 
-TOL = {("f32", "f32"): 1e-5, ("bf16", "bf16"): 1e-2, ("bf16", "fp8"): 3e-2}
+TOL = {("f32", "f32"): 1e-5, ("bf16", "bf16"): 1e-2, ("bf16", "fp8"): 3e-2,
+       ("bf16", "mxfp4"): 1e-2}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -152,6 +153,13 @@ SMALL = {
     "bf16_router_gemm_odd_E": synth.WORKLOADS["prefill"].replace(
         name="bf16_T1030_d256_E130_k3_F128_zipf", T=1030, d=256, E=130, num_local=130, k=3,
         F=128, seed=32),
+    # MXFP4 weights: decode tiles (ragged N tiles of 128 features), and the
+    # 128 x 512 tiles on an expert-parallel block with a half-filled N tile
+    "mxfp4_decode_tiles": synth.WORKLOADS["decode_mxfp4"].replace(
+        name="mxfp4_T200_d256_E16_k4_F384", T=200, d=256, E=16, num_local=16, k=4, F=384, seed=33),
+    "mxfp4_prefill_rank": synth.WORKLOADS["decode_mxfp4"].replace(
+        name="mxfp4_T2000_d512_E16_local4-11_k4_F384_zipf", T=2000, d=512, E=16, num_local=8,
+        expert_begin=4, k=4, F=384, bias=("zipf", 1.1, 2.0), seed=34, regime="prefill"),
     # f32 with more tiles than the tiny workload
     "f32_tiles": synth.WORKLOADS["tiny"].replace(
         name="f32_T300_d256_E8_k3_F384", T=300, d=256, E=8, num_local=8, k=3, F=384, seed=26),
@@ -184,6 +192,11 @@ MULTI = {
     "fp8_decode_plan": synth.WORKLOADS["dsv3_rank"].replace(
         name="fp8_T64_d512_E32_local0-15_k4_F512", T=64, d=512, E=32, num_local=16,
         expert_begin=0, k=4, F=512, seed=65),
+    "mxfp4_decode_plan": synth.WORKLOADS["decode_mxfp4"].replace(
+        name="mxfp4_T40_d512_E16_k4_F512", T=40, d=512, E=16, num_local=16, k=4, F=512, seed=68),
+    "mxfp4_plan": synth.WORKLOADS["decode_mxfp4"].replace(
+        name="mxfp4_T1500_d512_E16_local4-11_k4_F512", T=1500, d=512, E=16, num_local=8,
+        expert_begin=4, k=4, F=512, seed=69, regime="prefill"),
 }
 
 
@@ -211,6 +224,19 @@ def test_fp8_zero_and_spread_block_scales(case):
         f = torch.exp2(torch.randint(-8, 9, s.shape, generator=g).float())
         f[torch.rand(s.shape, generator=g) < 0.15] = 0.0
         setattr(pr, n, (s * f).contiguous())
+    check(pr, forward(pr))
+
+
+@pytest.mark.parametrize("case", ["mxfp4_plan", "mxfp4_decode_plan"])
+def test_mxfp4_spread_scales(case):
+    """E8M0 scales moved by up to 2^8 either way per (32-value block, row): a
+    scale read for the wrong row or K block cannot pass."""
+    pr = synth.make_problem(MULTI[case].replace(name=case + "_scales", seed=71))
+    g = torch.Generator().manual_seed(72)
+    for n in ("s_gate", "s_up", "s_down"):
+        s = getattr(pr, n).to(torch.int32)
+        s = (s + torch.randint(-8, 9, s.shape, generator=g, dtype=torch.int32)).clamp(0, 252)
+        setattr(pr, n, s.to(torch.uint8).contiguous())
     check(pr, forward(pr))
 
 
@@ -352,7 +378,7 @@ def test_batch_sweep_parity(T):
 
 
 @pytest.mark.parametrize("name,n_sample", [("decode", None), ("prefill", 96), ("mixtral", 32),
-                                           ("dsv3_rank", 48)])
+                                           ("dsv3_rank", 48), ("decode_mxfp4", None)])
 def test_full_size_workloads(name, n_sample):
     wl = synth.WORKLOADS[name]
     print(f"generating {wl.name}", flush=True)
