@@ -56,7 +56,7 @@ def gate_up_kernel_name(wl: synth.Workload) -> str:
         return "grouped_f32_kernel<true>"
     bits = W_BITS[wl.weight]
     if wl.weight == "mxfp4":
-        args = "1, 1, 2, 4, true, 4, 64, 8, 1" if S <= 64 * El else "2, 2, 4, 4, true, 4, 64, 4, 1"
+        args = "1, 1, 2, 4, true, 4, 128, 2, 3" if S <= 64 * El else "2, 2, 4, 4, true, 4, 64, 4, 1"
     elif S <= 16 * El or (S <= 64 * El and wl.weight == "fp8"):
         args = f"1, 1, 2, 4, true, {bits}, 64, 4, {2 if wl.weight == 'fp8' else 1}"
     elif S <= 64 * El:

@@ -223,28 +223,38 @@ struct Cfg {
   static constexpr int kStage = kStageA + kStageB + kStageS;
   static constexpr int kLoadsA = kStageA / (1024 * kWaves);  // 1 KB LDS-DMA loads per wave
   static constexpr int kLoadsB = kStageB / (1024 * kWaves);
-  static constexpr int kLoadsS = kFP4 ? 1 : 0;                // one 4-byte LDS-DMA per wave
-  static constexpr int kScaleLanes = kFP4 ? kStageS / (4 * kWaves) : 1;  // its active lanes
+  // MXFP4 scale loads: 4-byte LDS-DMAs of kScaleLanes lanes, each inside one
+  // K block and one weight matrix of the tile, kLoadsS per wave
+  static constexpr int kScaleHalf = kGateUp ? BNW / 2 : BNW;  // bytes of one matrix per K block
+  static constexpr int kScaleLanes =
+      !kFP4 ? 1
+            : (kScaleHalf / 4 < kWave ? kScaleHalf / 4 : kWave) < kStageS / (4 * kWaves)
+                  ? (kScaleHalf / 4 < kWave ? kScaleHalf / 4 : kWave)
+                  : kStageS / (4 * kWaves);
+  static constexpr int kLoadsS = kFP4 ? kStageS / (4 * kScaleLanes * kWaves) : 0;
   static constexpr int kLoads = kLoadsA + kLoadsB + kLoadsS;
   static constexpr int kSteps = kBK / 16;                     // MFMA K steps per stage
   static constexpr int kScaleSets = kFP8 ? BNW / 128 : 0;  // 128-row weight blocks per tile
   static constexpr int kMaxKBlocks = 65536 / 128;
   static constexpr int kLds = kStages * kStage + 2 * kScaleSets * kMaxKBlocks * 4;
-  static_assert(kBK == 32 || kBK == 64, "K step");
+  static_assert(kBK == 32 || kBK == 64 || (kFP4 && kBK == 128), "K step");
+  // MXFP4: 16-byte chunks (32 codes, one scale block) per lane, weight block
+  // and stage; a lane covers K values g kBK/2 .. (g + 1) kBK/2 - 1 of a stage
+  static constexpr int kFp4Chunks = kFP4 ? kBK / 64 : 1;
   static_assert(kStageA % (1024 * kWaves) == 0 && kStageB % (1024 * kWaves) == 0, "load split");
   static_assert(!kGateUp || NB % 2 == 0, "gate/up pairs column blocks");
   static_assert(kStages >= 2 && (kStages - 1) * kLoads < 64, "vmcnt budget");
   static_assert(kLds <= 160 * 1024, "LDS budget");
-  static_assert(128 % kBK == 0, "a scale block spans whole K steps");
+  static_assert(!kFP8 || 128 % kBK == 0, "a scale block spans whole K steps");
   static_assert(!kFP8 || (kGateUp ? (BNW / 2) % 128 == 0 : BNW % 128 == 0),
                 "FP8 scales: whole 128-row weight blocks per tile (per half for gate/up)");
   static_assert(!kFP8 || kBK == 64, "FP8 raw codes are double-buffered per step pair");
-  static_assert(!kFP4 || kBK == 64, "MXFP4: one 16-byte chunk (two 32-value scale blocks) per lane per stage");
-  static_assert(!kFP4 || (kScaleLanes >= 1 && kScaleLanes <= kWave &&
-                          kStageS == 4 * kScaleLanes * kWaves),
-                "MXFP4 scales: one dword LDS-DMA per wave covers the stage's scales");
-  static_assert(!kFP4 || (kGateUp ? (BNW / 2) : BNW) % (4 * kScaleLanes) == 0,
-                "MXFP4 scales: a wave's dwords lie in one K block and one weight matrix");
+  static_assert(!kFP4 || kBK == 64 || kBK == 128, "MXFP4: whole 32-value scale blocks per lane");
+  static_assert(!kFP4 || (kScaleLanes >= 1 && kScaleLanes <= kWave && kLoadsS >= 1 &&
+                          kStageS == 4 * kScaleLanes * kWaves * kLoadsS),
+                "MXFP4 scales: whole dword LDS-DMAs per wave cover the stage's scales");
+  static_assert(!kFP4 || kScaleHalf % (4 * kScaleLanes) == 0,
+                "MXFP4 scales: one load's dwords lie in one K block and one weight matrix");
   static_assert(kSteps % 2 == 0, "fragment buffers alternate by step");
 };
 
@@ -363,8 +373,8 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
   __amdgpu_buffer_rsrc_t rsA, rsB0, rsB1;  // A rows; gate or down weights; up weights
   uint32_t offA[C::kLoadsA];
   uint32_t offB[C::kLoadsB];
-  __amdgpu_buffer_rsrc_t rsS;  // MXFP4: the scale matrix this wave's scale loads read
-  uint32_t offS = 0;
+  __amdgpu_buffer_rsrc_t rsS[C::kLoadsS > 0 ? C::kLoadsS : 1];  // MXFP4 scale loads' matrices
+  uint32_t offS[C::kLoadsS > 0 ? C::kLoadsS : 1];
   // weight instruction i of this wave reads up rows (one half of the tile)
   auto b_up = [&](int i) -> bool {
     return kGateUp && ((wave * C::kLoadsB + i) * kWave) / C::kChunksB >= BNW / 2;
@@ -402,17 +412,20 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
       offB[i] = wrow * wrow_bytes + c * 16;
     }
     if constexpr (kFP4) {
-      // this wave's dword of a stage's scale block: K block kb of the stage,
-      // tile bytes [wb % BNW, + 4 kScaleLanes) (wave-uniform matrix and K
-      // block); lane l: features fo .. fo + 3 of that matrix
+      // scale load i of this wave: stage bytes [wb, wb + 4 kScaleLanes), inside
+      // K block kb of the stage and one matrix (wave-uniform); lane l:
+      // features fo .. fo + 3 of that matrix
       const uint32_t smat = (uint32_t)(a.K / 32) * a.Nout;  // bytes of one expert's scales
-      const int wb = wave * C::kScaleLanes * 4;
-      const int kb = wb / BNW;
-      const bool up = kGateUp && (wb % BNW) >= BNW / 2;
-      const int fo = (wb % BNW) - (up ? BNW / 2 : 0) + 4 * l;
-      rsS = buffer_rsrc(static_cast<const unsigned char*>(up ? a.S1 : a.S0) + (size_t)j * smat,
-                        smat);
-      offS = (uint32_t)kb * a.Nout + (uint32_t)min(n0 + fo, a.Nout - 4);
+#pragma unroll
+      for (int i = 0; i < C::kLoadsS; ++i) {
+        const int wb = (wave * C::kLoadsS + i) * C::kScaleLanes * 4;
+        const int kb = wb / BNW;
+        const bool up = kGateUp && (wb % BNW) >= BNW / 2;
+        const int fo = (wb % BNW) - (up ? BNW / 2 : 0) + 4 * l;
+        rsS[i] = buffer_rsrc(
+            static_cast<const unsigned char*>(up ? a.S1 : a.S0) + (size_t)j * smat, smat);
+        offS[i] = (uint32_t)kb * a.Nout + (uint32_t)min(n0 + fo, a.Nout - 4);
+      }
     }
   };
 
@@ -427,9 +440,11 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
         lds_dma16_buf(b_up(i) ? rsB1 : rsB0, offB[i], (uint32_t)(Q) * C::kRowB,                \
                       sb_ + C::kStageA + (wave * C::kLoadsB + i) * 1024);                       \
     if constexpr (kFP4) {                                                                       \
-      if (l < C::kScaleLanes)                                                                   \
-        lds_dma4_buf(rsS, offS, (uint32_t)(Q) * (kBK / 32) * a.Nout,                            \
-                     sb_ + C::kStageA + C::kStageB + wave * C::kScaleLanes * 4);               \
+      _Pragma("unroll") for (int i = 0; i < C::kLoadsS; ++i)                                    \
+        if (l < C::kScaleLanes)                                                                 \
+          lds_dma4_buf(rsS[i], offS[i], (uint32_t)(Q) * (kBK / 32) * a.Nout,                    \
+                       sb_ + C::kStageA + C::kStageB +                                          \
+                           (wave * C::kLoadsS + i) * C::kScaleLanes * 4);                       \
     }                                                                                           \
   } while (0)
 
@@ -471,8 +486,8 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
   // MXFP4: one 16-byte chunk (32 codes: K values 32 g .. 32 g + 31 of the
   // stage) and its block scale per weight block, by stage parity; step s
   // uses codes 8 s .. 8 s + 7
-  u32x4_t raw4[2][kFP4 ? NB : 1];
-  float sc4[2][kFP4 ? NB : 1];
+  u32x4_t raw4[2][kFP4 ? NB : 1][C::kFp4Chunks];
+  float sc4[2][kFP4 ? NB : 1][C::kFp4Chunks];
   // MXFP4: byte of this lane's weight row in a stage's scale block (feature
   // order inside the tile)
   auto srow = [&](int n) -> int {
@@ -482,7 +497,9 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
   auto read_frags = [&](int stage, int s, int buf) {
     const unsigned char* As = smem + (stage % kStages) * C::kStage;
     const unsigned char* Bs = As + C::kStageA;
-    const int cA = kFP4 ? (4 * g + s) : kFP8 ? (4 * (s >> 1) + 2 * g + (s & 1)) : (2 * s + g);
+    const int cA = kFP4   ? (g * (kBK / 16) + s)
+                   : kFP8 ? (4 * (s >> 1) + 2 * g + (s & 1))
+                          : (2 * s + g);
 #pragma unroll
     for (int m = 0; m < MB; ++m)
       af[buf][m] = *reinterpret_cast<const bf16x8_t*>(
@@ -492,9 +509,13 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
         const unsigned char* Ss = Bs + C::kStageB;
 #pragma unroll
         for (int n = 0; n < NB; ++n) {
-          raw4[stage & 1][n] = *reinterpret_cast<const u32x4_t*>(
-              Bs + lds_off<C::kRowB>(brow(n), g));
-          sc4[stage & 1][n] = e8m0_to_f32(Ss[g * BNW + srow(n)]);
+#pragma unroll
+          for (int c = 0; c < C::kFp4Chunks; ++c) {
+            const int q = g * C::kFp4Chunks + c;  // chunk of the row = scale block of the stage
+            raw4[stage & 1][n][c] = *reinterpret_cast<const u32x4_t*>(
+                Bs + lds_off<C::kRowB>(brow(n), q));
+            sc4[stage & 1][n][c] = e8m0_to_f32(Ss[q * BNW + srow(n)]);
+          }
         }
       }
     } else if constexpr (kFP8) {
@@ -583,7 +604,7 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
       for (int n = 0; n < NB; ++n) {
         bf16x8_t bfr;
         if constexpr (kFP4) {
-          bfr = e2m1x8_to_bf16x8(raw4[sp][n][s], sc4[sp][n]);
+          bfr = e2m1x8_to_bf16x8(raw4[sp][n][s >> 2][s & 3], sc4[sp][n][s >> 2]);
         } else if constexpr (kFP8) {
           u32x4_t r = raw8[(s >> 1) & 1][n];
           if (anyz && zblk[n]) r = u32x4_t{0u, 0u, 0u, 0u};
@@ -849,8 +870,8 @@ hipError_t launch_gemm(const GemmArgs& a, long long max_items, hipStream_t st) {
 // experts hold a few hundred rows (less M padding) or 256 x 256 when they hold
 // a thousand or more (fewer bytes staged per MFMA).  FP8 weights: eight waves
 // of 64 x 128 in 128 x 512 tiles, 64-deep K steps (one byte per code) and 3
-// stages.  MXFP4 weights: the 32 x 256 decode tile with 8 stages (a stage
-// holds a quarter of the bf16 weight bytes), else the FP8 tile shape with 4.
+// stages.  MXFP4 weights: the 32 x 256 decode tile with 128-deep K steps, 2
+// stages and three workgroups per CU, else the FP8 tile shape with 4 stages.
 enum class Plan { kF32, kDecode, kDecode64, kWide, kBig, kFp8, kDecodeFp4, kFp4 };
 
 Plan plan_of(const Shape& s) {
@@ -1034,13 +1055,14 @@ hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
       if (e == hipSuccess) e = launch_gemm<2, 4, 4, 2, false, 16, 32, 4, 1>(dn, mt * dn.n_tiles_n, st);
       break;
     case Plan::kDecodeFp4:
-      // 4-bit weights: a 32 x 256 tile streams a quarter of the bf16 bytes
-      // per stage, so eight stages keep as many bytes in flight
+      // 4-bit weights: 128-deep K steps and two stages, three workgroups per
+      // CU (measured: one workgroup with eight or twelve 64-deep stages
+      // streams at 2.4 TB/s, three with two 128-deep stages at 3.7 TB/s)
       gu.n_tiles_n = ntn(s.F, 128);
       dn.n_tiles_n = ntn(s.d, 256);
-      e = launch_gemm<1, 1, 2, 4, true, 4, 64, 8, 1>(gu, mt * gu.n_tiles_n, st);
+      e = launch_gemm<1, 1, 2, 4, true, 4, 128, 2, 3>(gu, mt * gu.n_tiles_n, st);
       if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-      if (e == hipSuccess) e = launch_gemm<1, 1, 2, 4, false, 4, 64, 8, 1>(dn, mt * dn.n_tiles_n, st);
+      if (e == hipSuccess) e = launch_gemm<1, 1, 2, 4, false, 4, 128, 2, 3>(dn, mt * dn.n_tiles_n, st);
       break;
     case Plan::kFp4:
       gu.n_tiles_n = ntn(s.F, 256);
