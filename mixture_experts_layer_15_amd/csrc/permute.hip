@@ -26,6 +26,29 @@
 namespace moe {
 namespace {
 
+// Inclusive prefix sum over the kThreads threads of a workgroup (thread
+// order): a shuffle scan inside each wave, then each wave adds the totals of
+// the waves before it (two barriers instead of one per doubling step).
+// Integer sums, so the result does not depend on the order of additions.
+// `wave_tot`: LDS scratch of kThreads / 64 elements.
+template <int kThreads, typename V>
+__device__ __forceinline__ V block_inclusive_scan(V v, V* wave_tot) {
+  const int l = lane_id();
+  const int w = threadIdx.x / kWave;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const V t = __shfl_up(v, o, kWave);
+    if (l >= o) v += t;
+  }
+  if (l == kWave - 1) wave_tot[w] = v;
+  __syncthreads();
+  V add = 0;
+  for (int q = 0; q < w; ++q) add += wave_tot[q];
+  __syncthreads();  // wave_tot may be reused by the caller
+  return v + add;
+}
+
+
 constexpr int kChunk = kPermuteChunk;   // slots per workgroup
 constexpr int kThreads = 256;
 constexpr int kRounds = kChunk / kThreads;
@@ -60,8 +83,7 @@ __global__ __launch_bounds__(kMaxExperts) void permute_scan_kernel(int El, int n
                                                                    int32_t* counts,
                                                                    int32_t* offsets, int bm,
                                                                    int4* tiles, int* ntiles) {
-  __shared__ int sums[kMaxExperts];
-  __shared__ int tsum[kMaxExperts];
+  __shared__ long long wave_tot[kMaxExperts / kWave];
   __shared__ int stage[kScanLds];
   const int e = threadIdx.x;
   const int pitch = nb + 1;
@@ -75,19 +97,12 @@ __global__ __launch_bounds__(kMaxExperts) void permute_scan_kernel(int El, int n
   if (e < El)
     for (int b = 0; b < nb; ++b) cnt += at(b);
   const int nt = (tiles && e < El) ? (cnt + bm - 1) / bm : 0;
-  sums[e] = cnt;
-  tsum[e] = nt;
-  __syncthreads();
-  // inclusive Hillis-Steele scans over the experts (slots and M tiles)
-  for (int o = 1; o < kMaxExperts; o <<= 1) {
-    const int v = e >= o ? sums[e - o] : 0;
-    const int u = e >= o ? tsum[e - o] : 0;
-    __syncthreads();
-    sums[e] += v;
-    tsum[e] += u;
-    __syncthreads();
-  }
-  const int excl = sums[e] - cnt;
+  // inclusive scans over the experts of the slots (low 32 bits) and the M
+  // tiles (high 32 bits): both totals stay below 2^31
+  const long long both = block_inclusive_scan<kMaxExperts>(
+      (long long)cnt | ((long long)nt << 32), wave_tot);
+  const int incl_s = (int)(both & 0xffffffffLL), incl_t = (int)(both >> 32);
+  const int excl = incl_s - cnt;
   if (e < El) {
     counts[e] = cnt;
     offsets[e] = excl;
@@ -97,12 +112,12 @@ __global__ __launch_bounds__(kMaxExperts) void permute_scan_kernel(int El, int n
       at(b) = run;
       run += c;
     }
-    const int tfirst = tsum[e] - nt;
+    const int tfirst = incl_t - nt;
     for (int i = 0; i < nt; ++i) tiles[tfirst + i] = make_int4(e, excl + i * bm, excl + cnt, 0);
   }
   if (e == El - 1) {
-    offsets[El] = sums[e];
-    if (tiles) *ntiles = tsum[e];
+    offsets[El] = incl_s;
+    if (tiles) *ntiles = incl_t;
   }
   if (staged) {
     __syncthreads();
@@ -167,7 +182,7 @@ __global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(
     int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos, int bm, int4* tiles, int* ntiles) {
   __shared__ int hist[kMaxExperts];
   __shared__ int base[kMaxExperts];
-  __shared__ int scan[kSmallThreads];
+  __shared__ int wave_tot[kSmallWaves];
   __shared__ int wcnt[kSmallWaves][kMaxExperts];
   const int tid = threadIdx.x;
   const int w = tid / kWave;
@@ -186,15 +201,8 @@ __global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(
   // exclusive scan of the counts (and of the M tiles per expert)
   const int cnt = tid < El ? hist[tid] : 0;
   const int nt = (cnt + bm - 1) / bm;
-  scan[tid] = cnt | (nt << 16);  // both fit: cnt <= 8192, nt <= 8192
-  __syncthreads();
-  for (int o = 1; o < kSmallThreads; o <<= 1) {
-    const int v = tid >= o ? scan[tid - o] : 0;
-    __syncthreads();
-    scan[tid] += v;
-    __syncthreads();
-  }
-  const int incl = scan[tid];
+  // both sums fit 16 bits: at most 8192 slots and 8192 + El tiles
+  const int incl = block_inclusive_scan<kSmallThreads>(cnt | (nt << 16), wave_tot);
   const int off = (incl & 0xffff) - cnt;
   const int tfirst = (incl >> 16) - nt;
   if (tid < El) {

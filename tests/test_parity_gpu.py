@@ -267,6 +267,40 @@ def test_logits_input_mode_with_planted_ties():
     check(pr, gpu, check_logits=False)
 
 
+def test_non_finite_logits_still_give_valid_distinct_ids():
+    """Logits are expected finite; rows holding NaN or +-inf must still route
+    every slot to k distinct experts in [0, E) (NaN ranks as -inf), and the
+    finite rows must be unaffected."""
+    wl = synth.WORKLOADS["decode"].replace(name="nonfinite", T=96, d=256, E=32, num_local=32,
+                                           k=4, F=256)
+    pr = synth.make_problem(wl, seed=44)
+    g = torch.Generator().manual_seed(45)
+    L = torch.randn((wl.T, wl.E), generator=g)
+    bad = [3, 17, 40, 41, 95]
+    L[3, :] = float("nan")                      # all NaN: the k lowest ids
+    L[17, 5] = float("nan")                     # one NaN: ranked last
+    L[40, 7] = float("inf")                     # +inf: chosen first
+    L[41, :] = float("-inf")
+    L[95, ::2] = float("nan")
+    gpu = forward(pr, logits_in=L)
+    ids = gpu["topk_idx"].numpy()
+    assert ((ids >= 0) & (ids < wl.E)).all()
+    assert all(len(set(r.tolist())) == wl.k for r in ids)
+    assert ids[3].tolist() == [0, 1, 2, 3] and ids[41].tolist() == [0, 1, 2, 3]
+    assert 5 not in ids[17].tolist() and ids[40, 0] == 7
+    assert all(i % 2 == 1 for i in ids[95].tolist())
+    # finite rows: routing and outputs as the oracle gives them (rows are
+    # independent, so the non-finite rows are replaced by zeros there)
+    good = np.array([t for t in range(wl.T) if t not in bad])
+    Lz = L.clone()
+    Lz[bad] = 0.0
+    ref = oracle_for(pr, Lz, tokens=good)
+    assert np.array_equal(ids[good], ref["topk_idx"][good])
+    assert np.abs(gpu["topk_w"].numpy()[good] - ref["topk_w"][good]).max() <= 1e-6
+    err = rel_l2(gpu["out"].float().numpy()[good], ref["out"])
+    assert err <= TOL[(wl.act, wl.weight)]
+
+
 def test_all_equal_logits_pick_the_lowest_experts():
     wl = synth.WORKLOADS["decode"].replace(name="flat", T=64, d=128, E=16, num_local=16, k=5, F=128)
     pr = synth.make_problem(wl, seed=43)
