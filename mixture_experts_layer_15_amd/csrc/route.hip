@@ -341,7 +341,9 @@ __global__ __launch_bounds__(kThreads) void router_topk_kernel(const float* part
   const int l = lane_id();
   const int t = blockIdx.x * (kThreads / kWave) + w;
   if (t >= T) return;
-  constexpr int kBatch = 8;  // split partials loaded together
+  // split partials loaded together: all 16 splits of a decode batch in one
+  // round of loads when E <= 128
+  constexpr int kBatch = kPerLane <= 2 ? 16 : 8;
   float v[kPerLane];
 #pragma unroll
   for (int j = 0; j < kPerLane; ++j) v[j] = 0.f;
