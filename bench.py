@@ -64,9 +64,9 @@ def gate_up_kernel_name(wl: synth.Workload) -> str:
     elif wl.weight == "fp8":
         args = "2, 2, 4, 4, true, 8, 64, 3, 1"
     elif S >= 1024 * El:
-        args = "2, 4, 4, 2, true, 16, 32, 4, 1"
+        args = "2, 4, 4, 2, true, 16, 64, 2, 1"
     else:
-        args = "2, 2, 4, 4, true, 16, 32, 4, 1"
+        args = "2, 2, 4, 4, true, 16, 64, 2, 1"
     return f"grouped_gemm_kernel<{args}, false>"
 
 

@@ -875,9 +875,11 @@ hipError_t launch_gemm(const GemmArgs& a, long long max_items, hipStream_t st) {
 // waves side by side along N, 64-deep K steps, 4 stages; from 17 to 64 rows
 // per expert on average (bf16), 64 x 256 tiles, so that an expert's weights
 // are streamed by one M tile instead of two or three.  bf16 prefill: eight
-// waves of 64 x 128, 32-deep K steps and 4 stages, as 128 x 512 tiles when
+// waves of 64 x 128, 64-deep K steps and 2 stages, as 128 x 512 tiles when
 // experts hold a few hundred rows (less M padding) or 256 x 256 when they hold
-// a thousand or more (fewer bytes staged per MFMA).  FP8 weights: eight waves
+// a thousand or more (fewer bytes staged per MFMA).  (64-deep steps read whole
+// 128-byte lines of every row per stage and halve the barriers: 9-14 % faster
+// than 32-deep steps with 4 stages.)  FP8 weights: eight waves
 // of 64 x 128 in 128 x 512 tiles, 64-deep K steps (one byte per code) and 3
 // stages.  MXFP4 weights: the 32 x 256 decode tile with 128-deep K steps, 2
 // stages and three workgroups per CU, else the FP8 tile shape with 4 stages.
@@ -1052,16 +1054,16 @@ hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
     case Plan::kWide:
       gu.n_tiles_n = ntn(s.F, 256);
       dn.n_tiles_n = ntn(s.d, 512);
-      e = launch_gemm<2, 2, 4, 4, true, 16, 32, 4, 1>(gu, mt * gu.n_tiles_n, st);
+      e = launch_gemm<2, 2, 4, 4, true, 16, 64, 2, 1>(gu, mt * gu.n_tiles_n, st);
       if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-      if (e == hipSuccess) e = launch_gemm<2, 2, 4, 4, false, 16, 32, 4, 1>(dn, mt * dn.n_tiles_n, st);
+      if (e == hipSuccess) e = launch_gemm<2, 2, 4, 4, false, 16, 64, 2, 1>(dn, mt * dn.n_tiles_n, st);
       break;
     case Plan::kBig:
       gu.n_tiles_n = ntn(s.F, 128);
       dn.n_tiles_n = ntn(s.d, 256);
-      e = launch_gemm<2, 4, 4, 2, true, 16, 32, 4, 1>(gu, mt * gu.n_tiles_n, st);
+      e = launch_gemm<2, 4, 4, 2, true, 16, 64, 2, 1>(gu, mt * gu.n_tiles_n, st);
       if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-      if (e == hipSuccess) e = launch_gemm<2, 4, 4, 2, false, 16, 32, 4, 1>(dn, mt * dn.n_tiles_n, st);
+      if (e == hipSuccess) e = launch_gemm<2, 4, 4, 2, false, 16, 64, 2, 1>(dn, mt * dn.n_tiles_n, st);
       break;
     case Plan::kDecodeFp4:
       // 4-bit weights: 128-deep K steps and two stages, three workgroups per
