@@ -56,13 +56,13 @@ def gate_up_kernel_name(wl: synth.Workload) -> str:
         return "grouped_f32_kernel<true>"
     bits = W_BITS[wl.weight]
     if wl.weight == "mxfp4":
-        args = "1, 1, 2, 4, true, 4, 128, 2, 3" if S <= 64 * El else "2, 2, 4, 4, true, 4, 64, 4, 1"
+        args = "1, 1, 2, 4, true, 4, 128, 2, 3" if S <= 64 * El else "4, 1, 2, 8, true, 4, 64, 4, 1"
     elif S <= 16 * El or (S <= 64 * El and wl.weight == "fp8"):
         args = f"1, 1, 2, 4, true, {bits}, 64, 4, {2 if wl.weight == 'fp8' else 1}"
     elif S <= 64 * El:
         args = "2, 1, 2, 4, true, 16, 64, 4, 1"
     elif wl.weight == "fp8":
-        args = "2, 2, 4, 4, true, 8, 64, 3, 1"
+        args = "4, 1, 2, 8, true, 8, 64, 2, 1"
     elif S >= 1024 * El:
         args = "2, 4, 4, 2, true, 16, 64, 2, 1"
     else:

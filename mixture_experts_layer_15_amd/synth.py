@@ -79,6 +79,9 @@ WORKLOADS = {
     "decode_mxfp4": Workload("qwen3_30b_a3b_decode_T64_d2048_E128_k8_F768_mxfp4", T=64, d=2048,
                              E=128, k=8, F=768, expert_begin=0, num_local=128, act="bf16",
                              weight="mxfp4", seed=6, regime="decode"),
+    "prefill_mxfp4": Workload("qwen3_30b_a3b_prefill_T8192_d2048_E128_k8_F768_zipf1.1_mxfp4",
+                              T=8192, d=2048, E=128, k=8, F=768, expert_begin=0, num_local=128,
+                              act="bf16", weight="mxfp4", bias=("zipf", 1.1, 2.0), seed=7),
     "dsv3_rank": Workload("deepseek_v3_ep_rank_T16384_d7168_E256_local0-31_k8_F2048_fp8_zipf1.2",
                           T=16384, d=7168, E=256, k=8, F=2048, expert_begin=0, num_local=32,
                           act="bf16", weight="fp8", bias=("zipf", 1.2, 2.0), seed=5),

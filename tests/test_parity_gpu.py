@@ -4,7 +4,8 @@ Routing, counts, offsets, the permutation and slot positions must be equal bit
 for bit, given the library's own float32 logits (both sides decide on the same
 numbers; ties go to the lower expert index).  Gates must agree within 1e-6
 absolute, logits within 1e-5 relative L2 of the float64 logits, and the layer
-output within a relative L2 error of 1e-5 (float32), 1e-2 (bf16) or 3e-2 (bf16
+output within a relative L2 error of 1e-5 (float32), 1e-2 (bf16, and bf16
+activations with MXFP4 weights, which are widened exactly) or 3e-2 (bf16
 activations with FP8-E4M3 weights).  At the full workload sizes the output is
 compared on a seeded sample of tokens that the oracle evaluates one by one.
 """
@@ -412,7 +413,8 @@ def test_batch_sweep_parity(T):
 
 
 @pytest.mark.parametrize("name,n_sample", [("decode", None), ("prefill", 96), ("mixtral", 32),
-                                           ("dsv3_rank", 48), ("decode_mxfp4", None)])
+                                           ("dsv3_rank", 48), ("decode_mxfp4", None),
+                                           ("prefill_mxfp4", 64)])
 def test_full_size_workloads(name, n_sample):
     wl = synth.WORKLOADS[name]
     print(f"generating {wl.name}", flush=True)
