@@ -127,7 +127,7 @@ class HipEvents:
         return float(out.value)
 
 
-def measured_traffic(workload: str, kernel: str):
+def measured_traffic(workload: str, kernel: str, layout: str):
     """HBM bytes per dispatch of the dominant kernel from the committed
     rocprofv3 FETCH_SIZE/WRITE_SIZE runs (scaled by the copy-kernel
     calibration), or None when they were taken on other kernel sources or no
@@ -143,7 +143,8 @@ def measured_traffic(workload: str, kernel: str):
     if m.hexdigest() != rec["source_sha256"]:
         return None
     for r in rec["records"]:
-        if r["workload"] == workload and r["kernel"].startswith(kernel):
+        if (r["workload"] == workload and r["kernel"].startswith(kernel)
+                and r.get("weight_layout", "rows") == layout):
             return int(r["traffic_bytes_per_dispatch"])
     return None
 
@@ -194,19 +195,30 @@ def cpu_baseline(pr: synth.Problem, logits: torch.Tensor, budget_s: float) -> di
             "blas_threads": int(threads)}
 
 
-def measure(wl: synth.Workload, steps: int, warmup: int, copies: int, dev) -> dict:
+def measure(wl: synth.Workload, steps: int, warmup: int, copies: int, dev,
+            blocked: bool = False) -> dict:
     """Time `steps` moe_forward calls (after `warmup`) rotating `copies` weight
     copies, then the same steps with the library's stage events, then a warm
-    pass on one copy.  Returns times and the routing statistics."""
+    pass on one copy.  Returns times and the routing statistics.  blocked:
+    the weights are converted once (untimed, like a load-time conversion) to
+    the library's blocked layout."""
     pr = synth.make_problem(wl)
-    p = B.problem(wl.T, wl.d, wl.E, wl.k, wl.F, wl.expert_begin, wl.num_local, wl.act, wl.weight)
+    p = B.problem(wl.T, wl.d, wl.E, wl.k, wl.F, wl.expert_begin, wl.num_local, wl.act, wl.weight,
+                  blocked=blocked)
     x = pr.x.to(dev)
     wr = pr.w_router.to(dev)
     bias = None if pr.bias is None else pr.bias.to(dev)
     wsets = []
     for c in range(copies):
-        wsets.append({n: (None if getattr(pr, n) is None else getattr(pr, n).to(dev))
-                      for n in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")})
+        ws_ = {n: (None if getattr(pr, n) is None else getattr(pr, n).to(dev))
+               for n in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")}
+        if blocked:
+            for n, which in (("w_gate", 0), ("w_up", 0), ("w_down", 1)):
+                dst = torch.empty_like(ws_[n])
+                B.moe_pack_weights(p, which, ws_[n], dst)
+                ws_[n] = dst
+            torch.cuda.synchronize()
+        wsets.append(ws_)
     out = torch.empty((wl.T, wl.d), dtype=pr.x.dtype, device=dev)
     logits = torch.empty((wl.T, wl.E), dtype=torch.float32, device=dev)
     counts = torch.empty((wl.num_local,), dtype=torch.int32, device=dev)
@@ -428,6 +440,9 @@ def main() -> None:
     ap.add_argument("--weight-copies", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layout", default="blocked", choices=("rows", "blocked"),
+                    help="expert weight layout: converted once (untimed, as at model load) to "
+                         "the library's blocked layout (default), or row-major")
     ap.add_argument("--eplb", default=None,
                     help="comma-separated redundant-expert counts: EPLB placements of the "
                          "DeepSeek-V3 layer on 8 ranks (one JSON line per placement)")
@@ -457,7 +472,8 @@ def main() -> None:
     # at least four weight copies rotate through the steps, so that no step
     # finds a previous step's weights in the 256 MB Infinity Cache
     copies = args.weight_copies or 4
-    m = measure(wl, steps, warmup, copies, dev)
+    blocked = args.layout == "blocked" and wl.weight != "f32"
+    m = measure(wl, steps, warmup, copies, dev, blocked)
     pr, cnt = m["pr"], m["counts"]
     alg = algorithmic(wl, cnt, m["tokens_read"])
     ms_per_step, stage_ms = m["ms_per_step"], m["stage_ms"]
@@ -476,7 +492,7 @@ def main() -> None:
         if wl.weight == "fp8":
             roof["frac_of_fp8_peak"] = round(achieved / PEAK_FP8_TFLOPS, 4)
     roof["kernel"] = gate_up_kernel_name(wl)
-    roof["traffic"] = measured_traffic(wl.name, roof["kernel"])
+    roof["traffic"] = measured_traffic(wl.name, roof["kernel"], "blocked" if blocked else "rows")
     roof["kernel_ms"] = round(stage_ms["gate_up"], 5)
     roof["bytes_per_launch"] = alg["gu_bytes"]
     roof["flop_per_launch"] = alg["gu_flop"]
@@ -520,6 +536,7 @@ def main() -> None:
         "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "E": wl.E, "k": wl.k, "F": wl.F,
                    "local_experts": f"{wl.expert_begin}-{wl.expert_begin + wl.num_local - 1}",
                    "act": wl.act, "weights": wl.weight, "weight_copies": copies,
+                   "weight_layout": "blocked" if blocked else "rows",
                    "parallelism": "single GPU (all experts local)" if wl.num_local == wl.E
                    else "one expert-parallel rank's expert block"},
         "layer": layer,

@@ -107,13 +107,21 @@ typedef enum {
   MOE_CALL_ROUTE = 3
 } moe_call_t;
 
+/* Layout of the expert weight matrices. */
+typedef enum {
+  MOE_LAYOUT_ROWS = 0,    /* "out x in" row-major, as described above */
+  MOE_LAYOUT_BLOCKED = 1  /* the blocked layout written by moe_pack_weights */
+} moe_layout_t;
+
 /* Problem shape.  T tokens, hidden size d, E global experts, top-k, SwiGLU
  * width F, local expert block [expert_begin, expert_begin + num_local);
- * act / weight hold moe_dtype_t values. */
+ * act / weight hold moe_dtype_t values, weight_layout a moe_layout_t
+ * (MOE_LAYOUT_BLOCKED needs BF16, FP8_E4M3 or MXFP4 weights). */
 typedef struct {
   int32_t T, d, E, k, F;
   int32_t expert_begin, num_local;
   int32_t act, weight;
+  int32_t weight_layout;
 } moe_problem_t;
 
 /* Bytes of scratch `call` needs for problem p (0 if p is invalid).  The
@@ -279,6 +287,22 @@ moe_status_t moe_eplb_plan(const int64_t* load, int32_t E, int32_t G, int32_t R,
 moe_status_t moe_eplb_remap(int32_t T, int32_t k, int32_t E, int32_t G, const int32_t* topk_idx,
                             const int32_t* replicas, const int32_t* log_to_phys,
                             int32_t* topk_phys, void* stream);
+
+/* Blocked weight layout (for callers that convert weights once at load
+ * time): each expert matrix [Nout][K] is stored as [Nout/32][K/64] units of
+ * 32 rows x 64 K values, every unit holding exactly the bytes the expert
+ * GEMMs stage into LDS for that block (rows in the MFMA's feature order,
+ * 16-byte chunks XOR-swizzled), so that each stage of a weight block streams
+ * as one contiguous run instead of 32 separate row pieces.  Same size as the
+ * row-major matrix; the scales keep their layouts.  The results of every
+ * call are bit-identical to the row-major layout.
+ *  which: 0 = a gate or up matrix set [E_l][F][d] (call once for each),
+ *         1 = the down matrix set [E_l][d][F].
+ *  src, dst: device arrays of the matrix set's size (distinct).  The weight
+ *  format is p->weight (BF16, FP8_E4M3 or MXFP4); p->weight_layout is
+ *  ignored. */
+moe_status_t moe_pack_weights(const moe_problem_t* p, int32_t which, const void* src, void* dst,
+                              void* stream);
 
 #ifdef __cplusplus
 }

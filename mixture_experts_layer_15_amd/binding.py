@@ -20,6 +20,7 @@ MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMA
 MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4 = range(4)
 MOE_CALL_PERMUTE, MOE_CALL_EXPERT_FFN, MOE_CALL_FORWARD, MOE_CALL_ROUTE = range(4)
 MOE_FORWARD_EVENTS = 7
+MOE_LAYOUT_ROWS, MOE_LAYOUT_BLOCKED = range(2)
 
 FMT = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3, "mxfp4": MOE_MXFP4}
 
@@ -32,7 +33,8 @@ class MoEError(RuntimeError):
 
 class Problem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("T", "d", "E", "k", "F", "expert_begin", "num_local", "act", "weight")]
+                ("T", "d", "E", "k", "F", "expert_begin", "num_local", "act", "weight",
+                 "weight_layout")]
 
 
 class ForwardArgs(ctypes.Structure):
@@ -69,18 +71,21 @@ def load_library() -> ctypes.CDLL:
                         ctypes.POINTER(ctypes.c_double))
     lib.moe_eplb_plan.argtypes = [i64p, i32, i32, i32, i32p, i32p, i32p, f64p]
     lib.moe_eplb_remap.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
+    lib.moe_pack_weights.argtypes = [P, i32, vp, vp, vp]
     for f in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
-              "moe_eplb_plan", "moe_eplb_remap"):
+              "moe_eplb_plan", "moe_eplb_remap", "moe_pack_weights"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
 
 
-def problem(T, d, E, k, F, expert_begin=0, num_local=None, act="bf16", weight="bf16") -> Problem:
+def problem(T, d, E, k, F, expert_begin=0, num_local=None, act="bf16", weight="bf16",
+            blocked=False) -> Problem:
     num_local = E - expert_begin if num_local is None else num_local
     return Problem(T, d, E, k, F, expert_begin, num_local,
                    FMT[act] if isinstance(act, str) else act,
-                   FMT[weight] if isinstance(weight, str) else weight)
+                   FMT[weight] if isinstance(weight, str) else weight,
+                   MOE_LAYOUT_BLOCKED if blocked else MOE_LAYOUT_ROWS)
 
 
 def _ptr(t) -> Optional[int]:
@@ -185,6 +190,13 @@ def moe_eplb_remap(T, k, E, G, topk_idx, replicas, log_to_phys, topk_phys, strea
     st = load_library().moe_eplb_remap(T, k, E, G, _ptr(topk_idx), _ptr(replicas),
                                        _ptr(log_to_phys), _ptr(topk_phys), _stream(stream))
     _check("moe_eplb_remap", st)
+
+
+def moe_pack_weights(p, which: int, src, dst, stream=None) -> None:
+    """Blocked layout of one expert matrix set (which 0: gate or up, 1: down)."""
+    st = load_library().moe_pack_weights(ctypes.byref(p), which, _ptr(src), _ptr(dst),
+                                         _stream(stream))
+    _check("moe_pack_weights", st)
 
 
 def workspace(p: Problem, call: int, device="cuda") -> torch.Tensor:

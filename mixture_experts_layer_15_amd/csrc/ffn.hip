@@ -83,6 +83,7 @@ struct GemmArgs {
   int Nout;                    // output columns
   int n_tiles_n;               // N tiles per M tile
   int group_m;                 // M tiles per rasterization group (>= 1)
+  int blocked;                 // W0/W1 in the blocked layout (units of 32 rows x 64 K)
 };
 
 // ---- LDS layout of the pipeline stages
@@ -419,6 +420,23 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
       const uint32_t wrow = (uint32_t)min(n0 + feat_of_row(rr), a.Nout - 1);
       offB[i] = wrow * wrow_bytes + c * 16;
     }
+    if constexpr (kBK == 64 && !kRouter) {
+     if (a.blocked) {
+      // blocked weights: a stage's image of 32-row block b is one contiguous
+      // unit of 32 x kRowB bytes, so lane l of load i copies the bytes at the
+      // same position of that unit; a row block spans all K stages
+      constexpr uint32_t kUnit = 32u * C::kRowB;
+      const uint32_t rb_bytes = (uint32_t)nK * kUnit;
+#pragma unroll
+      for (int i = 0; i < C::kLoadsB; ++i) {
+        const uint32_t o = (uint32_t)((wave * C::kLoadsB + i) * 1024 + 16 * l);
+        int b = (int)(o / kUnit);
+        if (kGateUp && b >= BNW / 64) b -= BNW / 64;
+        const int rb = min(n0 / 32 + b, a.Nout / 32 - 1);
+        offB[i] = (uint32_t)rb * rb_bytes + o % kUnit;
+      }
+     }
+    }
     if constexpr (kFP4) {
       // scale load i of this wave: stage bytes [wb, wb + 4 kScaleLanes), inside
       // K block kb of the stage and one matrix (wave-uniform); lane l:
@@ -446,7 +464,7 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
         lds_dma16_buf(rsA, offA[i], (uint32_t)(qq_) * kBK * 2,                                    \
                       sb_ + (wave * C::kLoadsA + i) * 1024);                                    \
     _Pragma("unroll") for (int i = 0; i < C::kLoadsB; ++i)                                      \
-        lds_dma16_buf(b_up(i) ? rsB1 : rsB0, offB[i], (uint32_t)(qq_) * C::kRowB,                \
+        lds_dma16_buf(b_up(i) ? rsB1 : rsB0, offB[i], (uint32_t)(qq_) * bstage,                  \
                       sb_ + C::kStageA + (wave * C::kLoadsB + i) * 1024);                       \
     if constexpr (kFP4) {                                                                       \
       _Pragma("unroll") for (int i = 0; i < C::kLoadsS; ++i)                                    \
@@ -456,6 +474,9 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
                            (wave * C::kLoadsS + i) * C::kScaleLanes * 4);                       \
     }                                                                                           \
   } while (0)
+
+  // weight bytes between consecutive K stages of one row
+  const uint32_t bstage = a.blocked ? 32u * C::kRowB : (uint32_t)C::kRowB;
 
   int item = it_begin + slot;
   if (item >= it_end) return;
@@ -1011,6 +1032,7 @@ hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
   // decode tiles (about one M tile per expert) gain nothing from grouping and
   // stream best in plain M-major order; prefill tiles group 8 M tiles
   gu.group_m = dn.group_m = use_decode_tiles(s) ? 1 : 8;
+  gu.blocked = dn.blocked = s.blocked;
   if (s.weight == kF32) {
     gu.n_tiles_n = (s.F + kF32BN - 1) / kF32BN;
     dn.n_tiles_n = (s.d + kF32BN - 1) / kF32BN;
@@ -1074,9 +1096,15 @@ hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
       // streams at 2.4 TB/s, three with two 128-deep stages at 3.7 TB/s)
       gu.n_tiles_n = ntn(s.F, 128);
       dn.n_tiles_n = ntn(s.d, 256);
-      e = launch_gemm<1, 1, 2, 4, true, 4, 128, 2, 3>(gu, mt * gu.n_tiles_n, st);
-      if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-      if (e == hipSuccess) e = launch_gemm<1, 1, 2, 4, false, 4, 128, 2, 3>(dn, mt * dn.n_tiles_n, st);
+      if (s.blocked) {  // blocked units are 64 K deep
+        e = launch_gemm<1, 1, 2, 4, true, 4, 64, 3, 3>(gu, mt * gu.n_tiles_n, st);
+        if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
+        if (e == hipSuccess) e = launch_gemm<1, 1, 2, 4, false, 4, 64, 3, 3>(dn, mt * dn.n_tiles_n, st);
+      } else {
+        e = launch_gemm<1, 1, 2, 4, true, 4, 128, 2, 3>(gu, mt * gu.n_tiles_n, st);
+        if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
+        if (e == hipSuccess) e = launch_gemm<1, 1, 2, 4, false, 4, 128, 2, 3>(dn, mt * dn.n_tiles_n, st);
+      }
       break;
     case Plan::kFp4:
       gu.n_tiles_n = ntn(s.F, 256);
@@ -1090,6 +1118,53 @@ hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
   }
   if (e == hipSuccess && ev) e = hipEventRecord(ev[2], st);
   return e;
+}
+
+namespace {
+
+// Blocked weight layout (see moe_internal.h): thread per 16-byte chunk of the
+// destination.  Unit (e, rb, ks) holds rows rb*32 + feat(r), r < 32, K values
+// ks*64 .. +64; its row r, physical chunk pc carries logical chunk
+// pc ^ ((r / R) % C) with R = 256 / row bytes, C = row bytes / 16 (the swizzle
+// the GEMMs use for a staged row).
+__global__ __launch_bounds__(256) void pack_weights_kernel(const uint4* __restrict__ src,
+                                                           uint4* __restrict__ dst, int Nout,
+                                                           int K, int row_bytes,
+                                                           long long n_chunks) {
+  const long long q = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= n_chunks) return;
+  const int C = row_bytes / 16;               // chunks per unit row
+  const int R = 256 / row_bytes;
+  const long long unit_chunks = 32LL * C;
+  const int nk = K / 64;
+  const long long u = q / unit_chunks;        // unit index (e, rb, ks)
+  const int in = (int)(q % unit_chunks);
+  const int r = in / C, pc = in % C;
+  const int ks = (int)(u % nk);
+  const long long erb = u / nk;               // e * (Nout / 32) + rb
+  const int row = (int)(erb % (Nout / 32)) * 32 +
+                  ((r & ~31) | (((r >> 2) & 1) << 4) | (((r >> 3) & 3) << 2) | (r & 3));
+  const long long e = erb / (Nout / 32);
+  const int c = pc ^ ((r / R) % C);
+  const long long src_chunk =
+      ((e * Nout + row) * (long long)(K / 64) + ks) * C + c;  // K/64 units of C chunks per row
+  dst[q] = src[src_chunk];
+}
+
+}  // namespace
+
+hipError_t pack_weights(const Shape& s, int which, const void* src, void* dst, hipStream_t st) {
+  const int Nout = which == 0 ? s.F : s.d;   // gate/up: [F][d]; down: [d][F]
+  const int K = which == 0 ? s.d : s.F;
+  const int wbits = s.weight == kBF16 ? 16 : s.weight == kFP8 ? 8 : 4;
+  const int row_bytes = 64 * wbits / 8;
+  const long long n_chunks = (long long)s.El * Nout * (K / 64) * (row_bytes / 16);
+  if (n_chunks == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((n_chunks + 255) / 256);
+  hipLaunchKernelGGL(pack_weights_kernel, dim3(blocks), dim3(256), 0, st,
+                     static_cast<const uint4*>(src), static_cast<uint4*>(dst), Nout, K, row_bytes,
+                     n_chunks);
+  return hipGetLastError();
 }
 
 }  // namespace moe

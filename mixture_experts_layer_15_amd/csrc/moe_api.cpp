@@ -26,7 +26,10 @@ moe_status_t check_problem(const moe_problem_t* p, Shape* s) {
   if (p->d % 128 != 0 || p->F % 128 != 0) return MOE_ERR_INVALID_ARGUMENT;
   if (p->act < MOE_F32 || p->act > MOE_MXFP4 || p->weight < MOE_F32 || p->weight > MOE_MXFP4)
     return MOE_ERR_INVALID_ARGUMENT;
+  if (p->weight_layout != MOE_LAYOUT_ROWS && p->weight_layout != MOE_LAYOUT_BLOCKED)
+    return MOE_ERR_INVALID_ARGUMENT;
   if (!supported_pair(p->act, p->weight)) return MOE_ERR_UNSUPPORTED;
+  if (p->weight_layout == MOE_LAYOUT_BLOCKED && p->weight == MOE_F32) return MOE_ERR_UNSUPPORTED;
   if (p->E > moe::kMaxExperts || p->d > 65536 || p->F > 65536) return MOE_ERR_UNSUPPORTED;
   const long long S = (long long)p->T * p->k;
   if (S >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
@@ -46,6 +49,7 @@ moe_status_t check_problem(const moe_problem_t* p, Shape* s) {
   s->El = p->num_local;
   s->act = p->act;
   s->weight = p->weight;
+  s->blocked = p->weight_layout == MOE_LAYOUT_BLOCKED;
   s->S = S;
   return MOE_OK;
 }
@@ -236,6 +240,17 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_forward_args_t* a, vo
   if (e == hipSuccess) e = moe::combine(s, y, pos, nullptr, a->out, strm);
   if (e == hipSuccess) e = mark(6);
   return from_hip(e);
+}
+
+moe_status_t moe_pack_weights(const moe_problem_t* p, int32_t which, const void* src, void* dst,
+                              void* stream) {
+  Shape s;
+  moe_status_t st = check_problem(p, &s);
+  if (st != MOE_OK) return st;
+  if (which != 0 && which != 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (s.weight == MOE_F32) return MOE_ERR_UNSUPPORTED;
+  if (src == nullptr || dst == nullptr || src == dst) return MOE_ERR_INVALID_ARGUMENT;
+  return from_hip(moe::pack_weights(s, which, src, dst, static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_eplb_plan(const int64_t* load, int32_t E, int32_t G, int32_t R,

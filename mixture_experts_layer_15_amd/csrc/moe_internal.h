@@ -17,6 +17,7 @@ constexpr int kPermuteChunk = 2048;   // slots per workgroup in the permutation 
 struct Shape {
   int T, d, E, k, F, e0, El;
   int act, weight;
+  int blocked;  // expert weights in the blocked layout of pack_weights
   long long S;
 };
 
@@ -68,6 +69,13 @@ hipError_t permute(const Shape& s, const int32_t* topk_idx, int32_t* counts, int
 // ---- combine.hip
 hipError_t combine(const Shape& s, const void* y, const int32_t* slot_pos, const float* topk_w,
                    void* out, hipStream_t st);
+
+// Blocked layout of one stored expert weight matrix [Nout][K] (any weight
+// format but float32): [Nout/32][K/64][32 rows][64 K values], each 32 x 64
+// unit being the LDS image the expert GEMMs stage for that block (rows in
+// the MFMA feature order, 16-byte chunks XOR-swizzled).  Same size as the
+// row-major matrix.
+hipError_t pack_weights(const Shape& s, int which, const void* src, void* dst, hipStream_t st);
 
 // ---- eplb.hip
 // The placement plan of moe_eplb_plan (arguments already checked).

@@ -77,6 +77,20 @@ def test_unsupported_format_pairs(lib, act, weight):
     assert st == B.MOE_ERR_UNSUPPORTED
 
 
+def test_weight_layout_checks(lib):
+    p = _p()
+    p.weight_layout = 2
+    assert lib.moe_combine(ctypes.byref(p), FAKE, FAKE, None, FAKE, None) == B.MOE_ERR_INVALID_ARGUMENT
+    p = _p(act="f32", weight="f32", blocked=True)
+    assert lib.moe_combine(ctypes.byref(p), FAKE, FAKE, None, FAKE, None) == B.MOE_ERR_UNSUPPORTED
+    p = _p()
+    assert lib.moe_pack_weights(ctypes.byref(p), 2, FAKE, FAKE + 256, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_pack_weights(ctypes.byref(p), 0, FAKE, FAKE, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_pack_weights(ctypes.byref(p), 0, None, FAKE, None) == B.MOE_ERR_INVALID_ARGUMENT
+    p = _p(act="f32", weight="f32")
+    assert lib.moe_pack_weights(ctypes.byref(p), 0, FAKE, FAKE + 256, None) == B.MOE_ERR_UNSUPPORTED
+
+
 def test_mxfp4_needs_its_scales(lib):
     p = _p(weight="mxfp4")
     ws = B.moe_workspace_size(p, B.MOE_CALL_EXPERT_FFN)
