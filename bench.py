@@ -45,7 +45,7 @@ W_BITS = {"f32": 32, "bf16": 16, "fp8": 8, "mxfp4": 4}
 
 
 
-def gate_up_kernel_name(wl: synth.Workload) -> str:
+def gate_up_kernel_name(wl: synth.Workload, blocked: bool = False) -> str:
     """The gate/up kernel the library launches for this workload, as a
     rocprofv3 kernel trace names it (the library's tile plan: 32-row decode
     tiles up to 16 slots per expert on average, 64-row ones up to 64 (FP8 and
@@ -56,7 +56,10 @@ def gate_up_kernel_name(wl: synth.Workload) -> str:
         return "grouped_f32_kernel<true>"
     bits = W_BITS[wl.weight]
     if wl.weight == "mxfp4":
-        args = "1, 1, 2, 4, true, 4, 128, 2, 3" if S <= 64 * El else "4, 1, 2, 8, true, 4, 64, 4, 1"
+        if S <= 64 * El:  # blocked weights are staged 64 K deep
+            args = "1, 1, 2, 4, true, 4, 64, 3, 3" if blocked else "1, 1, 2, 4, true, 4, 128, 2, 3"
+        else:
+            args = "4, 1, 2, 8, true, 4, 64, 4, 1"
     elif S <= 16 * El or (S <= 64 * El and wl.weight == "fp8"):
         args = f"1, 1, 2, 4, true, {bits}, 64, 4, {2 if wl.weight == 'fp8' else 1}"
     elif S <= 64 * El:
@@ -291,12 +294,14 @@ def sweep(args, dev) -> None:
     for T in [int(t) for t in args.sweep.split(",")]:
         wl = base.replace(name=f"qwen3_30b_a3b_T{T}_d2048_E128_k8_F768", T=T)
         steps = args.steps or (100 if T <= 512 else 20)
-        m = measure(wl, steps, args.warmup if args.warmup is not None else 5, 4, dev)
+        m = measure(wl, steps, args.warmup if args.warmup is not None else 5, 4, dev,
+                    args.layout == "blocked")
         alg = algorithmic(wl, m["counts"], m["tokens_read"])
         t = m["ms_per_step"] * 1e-3
         gu = m["stage_ms"]["gate_up"] * 1e-3
         print(json.dumps({
-            "sweep": "qwen3_30b_a3b_batch", "T": T, "touched_experts": alg["touched"],
+            "sweep": "qwen3_30b_a3b_batch", "T": T, "weight_layout": args.layout,
+            "touched_experts": alg["touched"],
             "kept_slots": alg["N"], "ms_per_step": round(m["ms_per_step"], 5),
             "tokens_per_s": round(T / t, 1),
             "layer": {"alg_bytes": alg["layer_bytes"], "alg_flop": alg["layer_flop"],
@@ -491,7 +496,7 @@ def main() -> None:
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
         if wl.weight == "fp8":
             roof["frac_of_fp8_peak"] = round(achieved / PEAK_FP8_TFLOPS, 4)
-    roof["kernel"] = gate_up_kernel_name(wl)
+    roof["kernel"] = gate_up_kernel_name(wl, blocked)
     roof["traffic"] = measured_traffic(wl.name, roof["kernel"], "blocked" if blocked else "rows")
     roof["kernel_ms"] = round(stage_ms["gate_up"], 5)
     roof["bytes_per_launch"] = alg["gu_bytes"]
