@@ -294,8 +294,11 @@ moe_status_t moe_eplb_remap(int32_t T, int32_t k, int32_t E, int32_t G, const in
  * GEMMs stage into LDS for that block (rows in the MFMA's feature order,
  * 16-byte chunks XOR-swizzled), so that each stage of a weight block streams
  * as one contiguous run instead of 32 separate row pieces.  Same size as the
- * row-major matrix; the scales keep their layouts.  The results of every
- * call are bit-identical to the row-major layout.
+ * row-major matrix; the scales keep their layouts.  Results equal those of
+ * the row-major layout bit for bit, except in the decode-sized plans (at
+ * most 64 slots per local expert with bf16 or MXFP4 weights), which sum the
+ * K products in another order on the two layouts (within the same
+ * tolerances).
  *  which: 0 = a gate or up matrix set [E_l][F][d] (call once for each),
  *         1 = the down matrix set [E_l][d][F].
  *  src, dst: device arrays of the matrix set's size (distinct).  The weight

@@ -380,16 +380,19 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
   auto b_up = [&](int i) -> bool {
     return kGateUp && ((wave * C::kLoadsB + i) * kWave) / C::kChunksB >= BNW / 2;
   };
-  // bf16 decode gate/up: each item starts its K loop at its own stage
-  // (rotation by expert and N tile), so that the workgroups streaming weights
-  // at the same time do not all read the same offset of their rows (measured:
-  // 2 % faster; no gain on the other plans).  The rotation is a function of the
-  // item only, so results do not depend on the grid.
+  // bf16 decode gate/up on row-major weights: each item starts its K loop at
+  // its own stage (rotation by expert and N tile), so that the workgroups
+  // streaming weights at the same time do not all read the same offset of
+  // their rows (measured: 2 % faster; on blocked weights, whose stages are
+  // contiguous runs, 3 % slower, and no gain on the other plans).  The
+  // rotation is a function of the item only, so results do not depend on the
+  // grid.
   constexpr bool kRotK = kGateUp && kWBits == 16 && C::BM <= 64 && !kRouter;
   int qrot = 0;
   auto set_src = [&](int j, int row0, int row_end, int n0, const int* rows) {
     j = __builtin_amdgcn_readfirstlane(j);
-    if constexpr (kRotK) qrot = __builtin_amdgcn_readfirstlane((j * 3 + n0 / 32) % nK);
+    if constexpr (kRotK)
+      if (!a.blocked) qrot = __builtin_amdgcn_readfirstlane((j * 3 + n0 / 32) % nK);
     row0 = __builtin_amdgcn_readfirstlane(row0);
     row_end = __builtin_amdgcn_readfirstlane(row_end);
     const uint32_t arow_bytes = (uint32_t)a.K * 2;
