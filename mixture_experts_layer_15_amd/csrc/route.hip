@@ -414,6 +414,89 @@ __global__ __launch_bounds__(kThreads) void router_topk_kernel(const float* part
     if (q * kWave + l < k) topk_w[(size_t)t * k + q * kWave + l] = mine[q] / tot;
 }
 
+// Maximum of a 64-bit key over each row of 16 lanes (DPP steps only): every
+// lane of the row ends with the row's maximum.
+__device__ __forceinline__ uint64_t row_max_u64(uint64_t key) {
+  auto dpp_step = [&](auto ctrl_tag) {
+    constexpr int kCtrl = decltype(ctrl_tag)::value;
+    const uint32_t lo = (uint32_t)key, hi = (uint32_t)(key >> 32);
+    const uint32_t plo = __builtin_amdgcn_update_dpp(0u, lo, kCtrl, 0xF, 0xF, false);
+    const uint32_t phi = __builtin_amdgcn_update_dpp(0u, hi, kCtrl, 0xF, 0xF, false);
+    const uint64_t p = ((uint64_t)phi << 32) | plo;
+    key = p > key ? p : key;
+  };
+  dpp_step(std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]: lane ^ 1
+  dpp_step(std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]: lane ^ 2
+  dpp_step(std::integral_constant<int, 0x141>{});  // row_half_mirror: the other quad of 8
+  dpp_step(std::integral_constant<int, 0x140>{});  // row_mirror: the other half of 16
+  return key;
+}
+
+// Many tokens: a row of 16 lanes per token (four tokens per wave), lane j of
+// the row holding experts j + 16 i (i < kPerLane), so that a selection round
+// is a local maximum over kPerLane keys and four DPP steps instead of a
+// wave-wide reduction per token.  Same sums, keys, ties and gates as
+// router_topk_kernel; k <= 16 (chosen i is kept by lane i of the row).
+template <int kPerLane>
+__global__ __launch_bounds__(kThreads) void router_topk_rows_kernel(
+    const float* part, int nsplit, const float* bias, float* logits_out, int T, int E, int k,
+    int32_t* topk_idx, float* topk_w) {
+  const int l = lane_id();
+  const int j = l & 15;  // lane in the token's row
+  const int t = (blockIdx.x * kThreads + threadIdx.x) / 16;
+  const bool live = t < T;  // every lane takes part in the row exchanges
+  float v[kPerLane];
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i) v[i] = 0.f;
+  for (int q = 0; q < nsplit; ++q) {
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) {
+      const int e = j + 16 * i;
+      const float pv = (live && e < E) ? part[((size_t)q * T + t) * E + e] : 0.f;
+      v[i] = q == 0 ? pv : v[i] + pv;
+    }
+  }
+  uint64_t key[kPerLane];
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i) {
+    const int e = j + 16 * i;
+    key[i] = 0;  // below every real key: never chosen
+    if (live && e < E) {
+      float s = v[i];
+      if (bias) s += bias[e];
+      if (logits_out) logits_out[(size_t)t * E + e] = s;
+      if (s != s) s = -INFINITY;  // NaN never wins (inputs are expected finite)
+      key[i] = select_key(s, e);
+    }
+  }
+  float first = 0.f, mine = 0.f;
+  int mine_e = 0;
+  for (int r = 0; r < k; ++r) {
+    uint64_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < kPerLane; ++i) best = key[i] > best ? key[i] : best;
+    best = row_max_u64(best);
+    // the owner retires the chosen expert (keys are distinct: they hold the id)
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i)
+      if (key[i] == best) key[i] = 0;
+    const float bv = key_value(best);
+    if (r == 0) first = bv;
+    if (r == j) {
+      mine = bv;
+      mine_e = (int)~(uint32_t)best;
+    }
+  }
+  float p = j < k ? expf(mine - first) : 0.f;
+  float tot = p;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) tot += __shfl_xor(tot, o, kWave);
+  if (live && j < k) {
+    topk_idx[(size_t)t * k + j] = mine_e;
+    topk_w[(size_t)t * k + j] = p / tot;
+  }
+}
+
 // W_r [d][E] -> [E][d] (bf16), 64 x 64 tiles through LDS with 16-byte global
 // accesses: the router kernels read each expert's weights as one contiguous
 // K row, like the expert GEMMs.
@@ -521,6 +604,23 @@ hipError_t route(const Shape& s, const void* x, const void* w_router, const floa
   }
   // (with one split the partials are `logits` itself: each lane reads its
   // elements, then writes the final values back)
+  if (s.T >= 1024 && s.k <= 16) {
+    // many tokens: four per wave
+    const dim3 rgrid((s.T + kThreads / 16 - 1) / (kThreads / 16));
+    if (s.E <= 64)
+      hipLaunchKernelGGL(router_topk_rows_kernel<4>, rgrid, dim3(kThreads), 0, st, part, nsplit,
+                         b, publish, s.T, s.E, s.k, topk_idx, topk_w);
+    else if (s.E <= 128)
+      hipLaunchKernelGGL(router_topk_rows_kernel<8>, rgrid, dim3(kThreads), 0, st, part, nsplit,
+                         b, publish, s.T, s.E, s.k, topk_idx, topk_w);
+    else if (s.E <= 256)
+      hipLaunchKernelGGL(router_topk_rows_kernel<16>, rgrid, dim3(kThreads), 0, st, part, nsplit,
+                         b, publish, s.T, s.E, s.k, topk_idx, topk_w);
+    else
+      hipLaunchKernelGGL(router_topk_rows_kernel<32>, rgrid, dim3(kThreads), 0, st, part, nsplit,
+                         b, publish, s.T, s.E, s.k, topk_idx, topk_w);
+    return hipGetLastError();
+  }
   const int wpb = kThreads / kWave;
   const dim3 tgrid((s.T + wpb - 1) / wpb);
   if (s.E <= 64)

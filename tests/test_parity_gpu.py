@@ -167,6 +167,10 @@ SMALL = {
     "bf16_router_gemm": synth.WORKLOADS["prefill"].replace(
         name="bf16_T1100_d384_E200_k6_F128_zipf", T=1100, d=384, E=200, num_local=200, k=6,
         F=128, seed=30),
+    # more than 256 experts: router top-k rows of 32 keys per lane
+    "bf16_router_E320": synth.WORKLOADS["prefill"].replace(
+        name="bf16_T1040_d256_E320_k5_F128_zipf", T=1040, d=256, E=320, num_local=320, k=5,
+        F=128, seed=37),
     "bf16_router_gemm_odd_E": synth.WORKLOADS["prefill"].replace(
         name="bf16_T1030_d256_E130_k3_F128_zipf", T=1030, d=256, E=130, num_local=130, k=3,
         F=128, seed=32),
@@ -174,6 +178,14 @@ SMALL = {
     # 128 x 512 tiles on an expert-parallel block with a half-filled N tile
     "mxfp4_decode_tiles": synth.WORKLOADS["decode_mxfp4"].replace(
         name="mxfp4_T200_d256_E16_k4_F384", T=200, d=256, E=16, num_local=16, k=4, F=384, seed=33),
+    # decode tiles on an expert-parallel block with d and F not multiples of
+    # 256 (bf16 and MXFP4)
+    "bf16_decode_rank": synth.WORKLOADS["decode"].replace(
+        name="bf16_T50_d384_E24_local6-17_k3_F640", T=50, d=384, E=24, num_local=12,
+        expert_begin=6, k=3, F=640, seed=35),
+    "mxfp4_decode_rank": synth.WORKLOADS["decode_mxfp4"].replace(
+        name="mxfp4_T60_d384_E24_local6-17_k3_F640", T=60, d=384, E=24, num_local=12,
+        expert_begin=6, k=3, F=640, seed=36),
     "mxfp4_prefill_rank": synth.WORKLOADS["decode_mxfp4"].replace(
         name="mxfp4_T2000_d512_E16_local4-11_k4_F384_zipf", T=2000, d=512, E=16, num_local=8,
         expert_begin=4, k=4, F=384, bias=("zipf", 1.1, 2.0), seed=34, regime="prefill"),
@@ -245,12 +257,12 @@ def test_fp8_zero_and_spread_block_scales(case):
 
 
 def same_plan_when_blocked(wl):
-    # the MXFP4 decode plan takes 128-deep K steps on row-major weights and
-    # 64-deep ones on blocked weights (the blocked units are 64 deep), and the
-    # bf16 decode gate/up GEMM rotates its K order on row-major weights only:
-    # the products are summed in another order there, so only parity holds
+    # decode-sized GEMMs sum the products in another order on the two layouts
+    # (bf16: the gate/up K loop is rotated on row-major weights only; MXFP4:
+    # wave-streamed 64-deep slices on blocked weights, staged 128-deep steps on
+    # row-major ones), so only parity holds there
     decode = wl.T * wl.k <= 64 * wl.num_local
-    return not (decode and wl.weight in ("mxfp4", "bf16"))
+    return not (decode and wl.weight in ("bf16", "mxfp4"))
 
 
 @pytest.mark.parametrize("case", list(MULTI))
@@ -270,6 +282,19 @@ def test_blocked_weight_layout(case, monkeypatch):
             assert torch.equal(rows[n], blocked[n]), n
     check(pr, blocked)
     monkeypatch.setenv("MOE_MI355X_MAX_WORKGROUPS", "8")
+    assert torch.equal(forward(pr, gb, blocked=True)["out"], blocked["out"])
+
+
+@pytest.mark.parametrize("case", ["mxfp4_decode_tiles", "mxfp4_decode_rank", "bf16_decode_rank"])
+def test_blocked_weight_layout_decode_shapes(case, monkeypatch):
+    """Blocked weights on the decode-sized cases (MXFP4: the wave-streamed
+    GEMMs, whose items wrap around the grid when it is capped), d and F not
+    multiples of 256, an expert-parallel block."""
+    pr = synth.make_problem(SMALL[case])
+    gb = pack(pr, upload(pr))
+    blocked = forward(pr, gb, blocked=True)
+    check(pr, blocked)
+    monkeypatch.setenv("MOE_MI355X_MAX_WORKGROUPS", "3")
     assert torch.equal(forward(pr, gb, blocked=True)["out"], blocked["out"])
 
 
