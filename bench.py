@@ -48,18 +48,20 @@ W_BITS = {"f32": 32, "bf16": 16, "fp8": 8, "mxfp4": 4}
 def gate_up_kernel_name(wl: synth.Workload, blocked: bool = False) -> str:
     """The gate/up kernel the library launches for this workload, as a
     rocprofv3 kernel trace names it (the library's tile plan: 32-row decode
-    tiles up to 16 slots per expert on average, 64-row ones up to 64 (FP8 and
-    MXFP4: the 32-row ones), then 128 x 512 tiles for FP8 and MXFP4, 256 x 256
-    from 1024 slots per expert, else 128 x 512)."""
+    tiles up to 16 slots per expert on average, 64-row ones up to 64 (FP8: the
+    32-row ones; MXFP4: the wave-streamed kernel on blocked weights, 32-row
+    tiles with 128-deep steps on row-major ones), then 128 x 512 tiles for FP8
+    and MXFP4, 256 x 256 from 1024 slots per expert, else 128 x 512)."""
     S, El = wl.T * wl.k, wl.num_local
     if wl.weight == "f32":
         return "grouped_f32_kernel<true>"
     bits = W_BITS[wl.weight]
     if wl.weight == "mxfp4":
-        if S <= 64 * El:  # blocked weights are staged 64 K deep
-            args = "1, 1, 2, 4, true, 4, 64, 3, 3" if blocked else "1, 1, 2, 4, true, 4, 128, 2, 3"
-        else:
-            args = "4, 1, 2, 8, true, 4, 64, 4, 1"
+        if S <= 64 * El:
+            if blocked:
+                return "stream_gemm_kernel<true, 4, 4, 2, 2>"
+            return "grouped_gemm_kernel<1, 1, 2, 4, true, 4, 128, 2, 3, false, false>"
+        args = "4, 1, 2, 8, true, 4, 64, 4, 1"
     elif S <= 16 * El or (S <= 64 * El and wl.weight == "fp8"):
         args = f"1, 1, 2, 4, true, {bits}, 64, 4, {2 if wl.weight == 'fp8' else 1}"
     elif S <= 64 * El:
@@ -70,7 +72,7 @@ def gate_up_kernel_name(wl: synth.Workload, blocked: bool = False) -> str:
         args = "2, 4, 4, 2, true, 16, 64, 2, 1"
     else:
         args = "2, 2, 4, 4, true, 16, 64, 2, 1"
-    return f"grouped_gemm_kernel<{args}, false>"
+    return f"grouped_gemm_kernel<{args}, false, {'true' if blocked else 'false'}>"
 
 
 def expert_bytes(d: int, F: int, wfmt: str, n_experts: int, with_scales: bool = True) -> int:

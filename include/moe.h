@@ -290,10 +290,12 @@ moe_status_t moe_eplb_remap(int32_t T, int32_t k, int32_t E, int32_t G, const in
 
 /* Blocked weight layout (for callers that convert weights once at load
  * time): each expert matrix [Nout][K] is stored as [Nout/32][K/64] units of
- * 32 rows x 64 K values, every unit holding exactly the bytes the expert
- * GEMMs stage into LDS for that block (rows in the MFMA's feature order,
- * 16-byte chunks XOR-swizzled), so that each stage of a weight block streams
- * as one contiguous run instead of 32 separate row pieces.  Same size as the
+ * 32 rows x 64 K values.  A unit is the sequence of 1 KB MFMA operand loads
+ * of one wave for that block (load q, lane l: 16 bytes of row
+ * 32*block + feat(l % 32), the bytes of K chunk 2q + l/32 of the unit, feat
+ * the GEMMs' permuted feature order inside a 32-row block), so a stage of a
+ * weight block streams as one contiguous run, and a wave's operand load, from
+ * LDS or straight from memory, is 1 KB contiguous.  Same size as the
  * row-major matrix; the scales keep their layouts.  Results equal those of
  * the row-major layout bit for bit, except in the decode-sized plans (at
  * most 64 slots per local expert with bf16 or MXFP4 weights), which sum the

@@ -264,10 +264,13 @@ struct Cfg {
 
 // kRouter: the router products x W_r as one segment of `rows` token rows,
 // A = x read row by row, W0 = the router matrix stored [E][d], float32 output.
+// kBlk: weights in the blocked layout (units of 32 rows x 64 K values, each
+// the image of the MFMA operand loads of one wave: see pack_weights_kernel).
 template <int MB, int WM, int NB, int WN, bool kGateUp, int kWBits, int kBK, int kStages,
-          int kMinBlocks, bool kRouter>
+          int kMinBlocks, bool kRouter, bool kBlk>
 __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel(GemmArgs a) {
   using C = Cfg<MB, WM, NB, WN, kGateUp, kWBits, kBK, kStages>;
+  static_assert(!kBlk || (kBK == 64 && !kRouter), "blocked units are 64 K deep");
   constexpr bool kFP8 = C::kFP8;
   constexpr bool kFP4 = C::kFP4;
   static_assert(kWBits == 16 || kFP8 || kFP4, "weight bits");
@@ -390,12 +393,11 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
   // contiguous runs, 3 % slower, and no gain on the other plans).  The
   // rotation is a function of the item only, so results do not depend on the
   // grid.
-  constexpr bool kRotK = kGateUp && kWBits == 16 && C::BM <= 64 && !kRouter;
+  constexpr bool kRotK = kGateUp && kWBits == 16 && C::BM <= 64 && !kRouter && !kBlk;
   int qrot = 0;
   auto set_src = [&](int j, int row0, int row_end, int n0, const int* rows) {
     j = __builtin_amdgcn_readfirstlane(j);
-    if constexpr (kRotK)
-      if (!a.blocked) qrot = __builtin_amdgcn_readfirstlane((j * 3 + n0 / 32) % nK);
+    if constexpr (kRotK) qrot = __builtin_amdgcn_readfirstlane((j * 3 + n0 / 32) % nK);
     row0 = __builtin_amdgcn_readfirstlane(row0);
     row_end = __builtin_amdgcn_readfirstlane(row_end);
     const uint32_t arow_bytes = (uint32_t)a.K * 2;
@@ -426,8 +428,7 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
       const uint32_t wrow = (uint32_t)min(n0 + feat_of_row(rr), a.Nout - 1);
       offB[i] = wrow * wrow_bytes + c * 16;
     }
-    if constexpr (kBK == 64 && !kRouter) {
-     if (a.blocked) {
+    if constexpr (kBlk) {
       // blocked weights: a stage's image of 32-row block b is one contiguous
       // unit of 32 x kRowB bytes, so lane l of load i copies the bytes at the
       // same position of that unit; a row block spans all K stages
@@ -441,7 +442,6 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
         const int rb = min(n0 / 32 + b, a.Nout / 32 - 1);
         offB[i] = (uint32_t)rb * rb_bytes + o % kUnit;
       }
-     }
     }
     if constexpr (kFP4) {
       // scale load i of this wave: stage bytes [wb, wb + 4 kScaleLanes), inside
@@ -482,7 +482,7 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
   } while (0)
 
   // weight bytes between consecutive K stages of one row
-  const uint32_t bstage = a.blocked ? 32u * C::kRowB : (uint32_t)C::kRowB;
+  constexpr uint32_t bstage = kBlk ? 32u * C::kRowB : (uint32_t)C::kRowB;
 
   int item = it_begin + slot;
   if (item >= it_end) return;
@@ -530,6 +530,14 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
     if (kGateUp) return (n < H ? 0 : BNW / 2) + feat_of_row(wn * H * 32 + (n % H) * 32 + (l & 31));
     return feat_of_row(wn * NB * 32 + n * 32 + (l & 31));
   };
+  // LDS offset of this lane's 16-byte weight chunk q (chunk pair: K values
+  // 16 q + 8 g .. + 8 of bf16, 32 q + 16 g .. + 16 of FP8, 32 g .. + 32 of
+  // MXFP4) of weight block n in a stage: row-major weights sit as swizzled
+  // rows, blocked ones as units of 1 KB operand loads (lane l at 16 l)
+  auto b_off = [&](int n, int q) -> int {
+    if constexpr (kBlk) return (brow(n) >> 5) * (32 * C::kRowB) + q * 1024 + 16 * l;
+    return lds_off<C::kRowB>(brow(n), 2 * q + g);
+  };
   auto read_frags = [&](int stage, int s, int buf) {
     const unsigned char* As = smem + (stage % kStages) * C::kStage;
     const unsigned char* Bs = As + C::kStageA;
@@ -549,7 +557,7 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
           for (int c = 0; c < C::kFp4Chunks; ++c) {
             const int q = g * C::kFp4Chunks + c;  // chunk of the row = scale block of the stage
             raw4[stage & 1][n][c] = *reinterpret_cast<const u32x4_t*>(
-                Bs + lds_off<C::kRowB>(brow(n), q));
+                Bs + (kBlk ? b_off(n, c) : lds_off<C::kRowB>(brow(n), q)));
             sc4[stage & 1][n][c] = e8m0_to_f32(Ss[q * BNW + srow(n)]);
           }
         }
@@ -558,14 +566,12 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
       if ((s & 1) == 0) {
 #pragma unroll
         for (int n = 0; n < NB; ++n)
-          raw8[(s >> 1) & 1][n] = *reinterpret_cast<const u32x4_t*>(
-              Bs + lds_off<C::kRowB>(brow(n), 2 * (s >> 1) + g));
+          raw8[(s >> 1) & 1][n] = *reinterpret_cast<const u32x4_t*>(Bs + b_off(n, s >> 1));
       }
     } else {
 #pragma unroll
       for (int n = 0; n < NB; ++n)
-        bf[buf][n] = *reinterpret_cast<const bf16x8_t*>(
-            Bs + lds_off<C::kRowB>(brow(n), 2 * s + g));
+        bf[buf][n] = *reinterpret_cast<const bf16x8_t*>(Bs + b_off(n, s));
     }
   };
 
@@ -915,15 +921,15 @@ __global__ __launch_bounds__(kWave* kStreamWaves, kMinBlocks) void stream_gemm_k
   const uint32_t row_bytes = (uint32_t)a.K * kWBits / 8;  // one full weight row
   const uint32_t unit_step = a.blocked ? 32u * C::kRowB : (uint32_t)C::kRowB;  // per 64 K
   const uint32_t wmat = (uint32_t)a.Nout * row_bytes;
+  // (blocked: chunk q of the unit's rows is the 1 KB operand load q, lane l
+  // at 16 l; row-major: row fr, K chunk 2 q + g)
   uint32_t voffW[kFP4 ? 1 : 4];
   if constexpr (kFP4) {
-    voffW[0] = a.blocked ? (uint32_t)(r * 32 + ((g ^ ((r >> 3) & 1)) << 4))
-                         : (uint32_t)fr * row_bytes + 16u * g;
+    voffW[0] = a.blocked ? 16u * l : (uint32_t)fr * row_bytes + 16u * g;
   } else {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      voffW[q] = a.blocked ? (uint32_t)(r * 128 + (((2 * q + g) ^ ((r >> 1) & 7)) << 4))
-                           : (uint32_t)fr * row_bytes + 16u * (2 * q + g);
+      voffW[q] = a.blocked ? 1024u * q + 16u * l : (uint32_t)fr * row_bytes + 16u * (2 * q + g);
   }
 
   // per-item state
@@ -1127,10 +1133,11 @@ int num_cu() {
 }
 
 template <int MB, int WM, int NB, int WN, bool kGateUp, int kWBits, int kBK, int kStages,
-          int kMinBlocks, bool kRouter = false>
-hipError_t launch_gemm(const GemmArgs& a, long long max_items, hipStream_t st) {
+          int kMinBlocks, bool kRouter, bool kBlk>
+hipError_t launch_gemm_l(const GemmArgs& a, long long max_items, hipStream_t st) {
   using C = Cfg<MB, WM, NB, WN, kGateUp, kWBits, kBK, kStages>;
-  auto kern = grouped_gemm_kernel<MB, WM, NB, WN, kGateUp, kWBits, kBK, kStages, kMinBlocks, kRouter>;
+  auto kern =
+      grouped_gemm_kernel<MB, WM, NB, WN, kGateUp, kWBits, kBK, kStages, kMinBlocks, kRouter, kBlk>;
   static bool attr = false;
   if (!attr) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1148,6 +1155,22 @@ hipError_t launch_gemm(const GemmArgs& a, long long max_items, hipStream_t st) {
   const size_t lds = (size_t)kStages * C::kStage + (C::kFP8 ? 2u * C::kScaleSets * (a.K / 128) * 4 : 0);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::kThreads), lds, st, a);
   return hipGetLastError();
+}
+
+// the kernel for the weight layout in a.blocked (blocked units are 64 K deep:
+// plans with other K steps take row-major weights only)
+template <int MB, int WM, int NB, int WN, bool kGateUp, int kWBits, int kBK, int kStages,
+          int kMinBlocks, bool kRouter = false>
+hipError_t launch_gemm(const GemmArgs& a, long long max_items, hipStream_t st) {
+  if constexpr (kBK == 64 && !kRouter) {
+    if (a.blocked)
+      return launch_gemm_l<MB, WM, NB, WN, kGateUp, kWBits, kBK, kStages, kMinBlocks, kRouter,
+                           true>(a, max_items, st);
+  } else {
+    if (a.blocked) return hipErrorInvalidValue;
+  }
+  return launch_gemm_l<MB, WM, NB, WN, kGateUp, kWBits, kBK, kStages, kMinBlocks, kRouter, false>(
+      a, max_items, st);
 }
 
 // Wave-streamed decode GEMMs: one item per wave, items spread over
@@ -1185,9 +1208,9 @@ hipError_t launch_stream(const GemmArgs& a, long long max_items, hipStream_t st)
 // bf16 one, so the per-stage wait and barrier dominated); else the FP8
 // prefill tile shape with 4 stages (0.63 -> 0.42 ms against the 2 x 4 wave
 // grid on the Qwen3 prefill).  bf16 decode stays staged: streamed bf16 blocks
-// (2 or 4 per wave, 4 to 8 slices ahead) took 173-179 us for the Qwen3
-// gate/up against 138.5, a 16-byte lane load covering 32 B of each of 32
-// rows per instruction where the staged DMA moves 1 KB runs.
+// (2 or 4 per wave, 4 to 8 slices ahead, 8 or 12 waves per CU) took
+// 137-142 us for the Qwen3 gate/up against 138-140 staged on the same box,
+// and their down GEMM 73-75 us against 72-74.
 enum class Plan { kF32, kDecode, kDecode64, kWide, kBig, kFp8, kDecodeFp4, kFp4 };
 
 Plan plan_of(const Shape& s) {
@@ -1410,11 +1433,12 @@ hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
 
 namespace {
 
-// Blocked weight layout (see moe_internal.h): thread per 16-byte chunk of the
-// destination.  Unit (e, rb, ks) holds rows rb*32 + feat(r), r < 32, K values
-// ks*64 .. +64; its row r, physical chunk pc carries logical chunk
-// pc ^ ((r / R) % C) with R = 256 / row bytes, C = row bytes / 16 (the swizzle
-// the GEMMs use for a staged row).
+// Blocked weight layout: thread per 16-byte chunk of the destination.  Unit
+// (e, rb, ks) covers rows rb*32 .. +32 and K values ks*64 .. +64; it is
+// C/2 operand loads of 1 KB (C = 16-byte chunks per unit row), load q, lane
+// l holding chunk 2q + l/32 of row rb*32 + feat(l % 32), the row the MFMA
+// operand of lane l reads (feat: the GEMMs' permuted feature order inside a
+// 32-row block).
 __global__ __launch_bounds__(256) void pack_weights_kernel(const uint4* __restrict__ src,
                                                            uint4* __restrict__ dst, int Nout,
                                                            int K, int row_bytes,
@@ -1422,18 +1446,18 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const uint4* __restri
   const long long q = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (q >= n_chunks) return;
   const int C = row_bytes / 16;               // chunks per unit row
-  const int R = 256 / row_bytes;
   const long long unit_chunks = 32LL * C;
   const int nk = K / 64;
   const long long u = q / unit_chunks;        // unit index (e, rb, ks)
   const int in = (int)(q % unit_chunks);
-  const int r = in / C, pc = in % C;
+  const int ld = in / 64, l = in % 64;        // operand load, lane
+  const int r = l & 31;
+  const int c = 2 * ld + (l >> 5);            // chunk of the unit row
   const int ks = (int)(u % nk);
   const long long erb = u / nk;               // e * (Nout / 32) + rb
   const int row = (int)(erb % (Nout / 32)) * 32 +
                   ((r & ~31) | (((r >> 2) & 1) << 4) | (((r >> 3) & 3) << 2) | (r & 3));
   const long long e = erb / (Nout / 32);
-  const int c = pc ^ ((r / R) % C);
   const long long src_chunk =
       ((e * Nout + row) * (long long)(K / 64) + ks) * C + c;  // K/64 units of C chunks per row
   dst[q] = src[src_chunk];
