@@ -364,7 +364,9 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
         // set sb: the tile's sb-th 128-row weight block (gate/up: gate blocks,
         // then up blocks)
         const int sb = o / KB, kb = o % KB;
-        constexpr int kHalf = kGateUp ? C::kScaleSets / 2 : C::kScaleSets;
+        constexpr int kHalf = (kGateUp ? C::kScaleSets / 2 : C::kScaleSets) > 0
+                                  ? (kGateUp ? C::kScaleSets / 2 : C::kScaleSets)
+                                  : 1;  // (FP8 only)
         const float* S = static_cast<const float*>((kGateUp && sb >= kHalf) ? a.S1 : a.S0);
         const int nblk = min(n0 / 128 + sb % kHalf, a.Nout / 128 - 1);
         lds_dma4(S + ((long long)j * (a.Nout / 128) + nblk) * KB + kb,
@@ -910,9 +912,12 @@ __global__ __launch_bounds__(kWave* kStreamWaves, kMinBlocks) void stream_gemm_k
   const int ntn = a.n_tiles_n;      // items per M tile
   const int n_items = *a.ntiles * ntn;
   const int stride = gridDim.x * kStreamWaves;
-  // items round-robin over the workgroups first, so that every CU gets the
-  // same number of busy waves
-  int it = blockIdx.x + gridDim.x * wave;
+  // item pairs (2p, 2p + 1: neighbouring N groups of one M tile, which share
+  // activation rows and the 128-byte lines of their scales) round-robin over
+  // the workgroups first, so that every CU gets the same number of busy
+  // waves; the two items of a pair run on two waves of one workgroup
+  // (measured: MXFP4 gate/up 3 % faster than single items round-robin)
+  int it = 2 * (blockIdx.x + gridDim.x * (wave >> 1)) + (wave & 1);
   if (it >= n_items) return;
 
   // per-lane constants: row r of a weight block holds feature fr (the
@@ -1173,8 +1178,8 @@ hipError_t launch_gemm(const GemmArgs& a, long long max_items, hipStream_t st) {
       a, max_items, st);
 }
 
-// Wave-streamed decode GEMMs: one item per wave, items spread over
-// kMinBlocks workgroups per CU (never more workgroups than items).
+// Wave-streamed decode GEMMs: one item per wave, item pairs spread over
+// kMinBlocks workgroups per CU (never more workgroups than pairs).
 template <bool kGateUp, int kWBits, int NB, int kD, int kMinBlocks>
 hipError_t launch_stream(const GemmArgs& a, long long max_items, hipStream_t st) {
   using C = StreamCfg<kGateUp, kWBits, NB, kD>;
@@ -1182,7 +1187,7 @@ hipError_t launch_stream(const GemmArgs& a, long long max_items, hipStream_t st)
   if ((a.K / C::kSliceK) % kD != 0 || a.Nout % (32 * (kGateUp ? NB / 2 : NB)) != 0)
     return hipErrorInvalidValue;
   long long grid = (long long)num_cu() * kMinBlocks;
-  if (max_items < grid) grid = max_items;
+  if ((max_items + 1) / 2 < grid) grid = (max_items + 1) / 2;
   if (const long long cap = max_workgroups(); cap > 0 && cap < grid) grid = cap;
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL((stream_gemm_kernel<kGateUp, kWBits, NB, kD, kMinBlocks>),
