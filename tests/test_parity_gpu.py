@@ -167,6 +167,11 @@ SMALL = {
     "bf16_router_gemm": synth.WORKLOADS["prefill"].replace(
         name="bf16_T1100_d384_E200_k6_F128_zipf", T=1100, d=384, E=200, num_local=200, k=6,
         F=128, seed=30),
+    # many tokens, E = 100 (not a multiple of 8): the staged router product
+    # with masked expert columns, top-k rows with padded lanes
+    "bf16_router_direct_E100": synth.WORKLOADS["prefill"].replace(
+        name="bf16_T1100_d256_E100_k4_F128_zipf", T=1100, d=256, E=100, num_local=100, k=4,
+        F=128, seed=38),
     # more than 256 experts: router top-k rows of 32 keys per lane
     "bf16_router_E320": synth.WORKLOADS["prefill"].replace(
         name="bf16_T1040_d256_E320_k5_F128_zipf", T=1040, d=256, E=320, num_local=320, k=5,
