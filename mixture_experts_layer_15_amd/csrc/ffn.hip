@@ -87,6 +87,12 @@ struct GemmArgs {
   int n_tiles_n;               // N tiles per M tile
   int group_m;                 // M tiles per rasterization group (>= 1)
   int blocked;                 // W0/W1 in the blocked layout (units of 32 rows x 64 K)
+  // wave-streamed GEMMs with the K range split (ksplit > 1): float32
+  // partial products [ksplit][rows][Nout] (gate/up: gate columns, then up
+  // columns), summed by split_reduce_kernel
+  int ksplit;
+  float* part;
+  int part_rows;
 };
 
 // ---- LDS layout of the pipeline stages
@@ -908,9 +914,10 @@ __global__ __launch_bounds__(kWave* kStreamWaves, kMinBlocks) void stream_gemm_k
   const int l = lane_id();
   const int g = l >> 5;   // which 8 of an MFMA step's 16 K values this lane holds
   const int r = l & 31;   // MFMA row (weights) and column (tokens) of this lane
-  const int nS = a.K / C::kSliceK;  // a multiple of kD (host)
-  const int ntn = a.n_tiles_n;      // items per M tile
-  const int n_items = *a.ntiles * ntn;
+  const int nsplit = a.ksplit;      // K ranges per (M tile, N group)
+  const int nS = a.K / C::kSliceK / nsplit;  // slices per item, a multiple of kD (host)
+  const int ntn = a.n_tiles_n;      // N groups per M tile
+  const int n_items = *a.ntiles * ntn * nsplit;
   const int stride = gridDim.x * kStreamWaves;
   // item pairs (2p, 2p + 1: neighbouring N groups of one M tile, which share
   // activation rows and the 128-byte lines of their scales) round-robin over
@@ -942,8 +949,10 @@ __global__ __launch_bounds__(kWave* kStreamWaves, kMinBlocks) void stream_gemm_k
   uint32_t voffA = 0, voffS = 0;
   uint32_t sW[NB];  // byte offset of block n's rows in its matrix
   uint32_t sS[NB];  // MXFP4: first feature of block n
+  int sbase = 0;    // first slice of the item's K range (a multiple of kD)
   auto setup = [&](int item, int4 t, int ss) {
-    const int grp = item % ntn;
+    const int grp = (item / nsplit) % ntn;
+    sbase = (item % nsplit) * nS;
     const int j = __builtin_amdgcn_readfirstlane(t.x);
     const int p = min(__builtin_amdgcn_readfirstlane(t.y) + r, __builtin_amdgcn_readfirstlane(t.z) - 1);
     const uint32_t arow = kGateUp ? (uint32_t)(ss / a.k) : (uint32_t)p;
@@ -973,6 +982,7 @@ __global__ __launch_bounds__(kWave* kStreamWaves, kMinBlocks) void stream_gemm_k
   uint32_t sb[kD][kFP4 ? NB : 1];
   // slice s of the item set up last into ring entry e (e = s mod kD)
   auto issue = [&](int s, int e) {
+    s += sbase;
     if constexpr (kFP4) {
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
@@ -1026,7 +1036,7 @@ __global__ __launch_bounds__(kWave* kStreamWaves, kMinBlocks) void stream_gemm_k
   auto tile_of = [&](int item) -> int4 {
     int opaque_zero;
     asm volatile("v_mov_b32 %0, 0" : "=v"(opaque_zero));
-    return item < n_items ? a.tiles[item / ntn + opaque_zero] : make_int4(0, 0, 1, 0);
+    return item < n_items ? a.tiles[item / nsplit / ntn + opaque_zero] : make_int4(0, 0, 1, 0);
   };
   auto slot_of = [&](int4 t) -> int { return a.sorted_slot[min(t.y + r, t.z - 1)]; };
   int4 tc = tile_of(it);
@@ -1059,7 +1069,7 @@ __global__ __launch_bounds__(kWave* kStreamWaves, kMinBlocks) void stream_gemm_k
     }
     // last turn of the ring: the next item's first slices take the freed
     // entries (the wait counts stay those of the steady loop)
-    const int grp_c = it % ntn;
+    const int grp_c = (it / nsplit) % ntn, sp_c = it % nsplit;
     const int row0 = __builtin_amdgcn_readfirstlane(tc.y), rend = __builtin_amdgcn_readfirstlane(tc.z);
     const float gate_c = gate;
     int ss_nn = 0;
@@ -1085,7 +1095,20 @@ __global__ __launch_bounds__(kWave* kStreamWaves, kMinBlocks) void stream_gemm_k
 
     // epilogue: register q of block n is feature 16 g + q of the block
     const int p = row0 + r;
-    if (p < rend) {
+    if (nsplit > 1) {
+      // float32 partial products of this K range (gate/up: gate, then up columns)
+      if (p < rend) {
+        float* prow = a.part + ((long long)sp_c * a.part_rows + p) * (kGateUp ? 2 * a.Nout : a.Nout);
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+          const int col = (kGateUp && n >= H ? a.Nout : 0) + grp_c * H * 32 + (n % H) * 32 + 16 * g;
+#pragma unroll
+          for (int q = 0; q < 16; q += 4)
+            *reinterpret_cast<f32x4_t*>(prow + col + q) =
+                f32x4_t{acc[n][q], acc[n][q + 1], acc[n][q + 2], acc[n][q + 3]};
+        }
+      }
+    } else if (p < rend) {
       uint16_t* orow = a.out + (long long)p * a.Nout;
 #pragma unroll
       for (int n = 0; n < H; ++n) {
@@ -1111,6 +1134,43 @@ __global__ __launch_bounds__(kWave* kStreamWaves, kMinBlocks) void stream_gemm_k
     tnn = tnnn;
     ss_n = ss_nn;
   }
+}
+
+// Sum of the K-range partial products in split order, then the epilogue of
+// the unsplit GEMM: gate/up h = silu(gate) * up, down y = sum * gate(row).
+// Thread per 8 output columns of a kept row (rows past offsets[El] are not
+// written: no tile covers them).
+template <bool kGateUp>
+__global__ __launch_bounds__(256) void split_reduce_kernel(GemmArgs a, int El) {
+  const int n8 = a.Nout / 8;
+  const long long o = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const int p = (int)(o / n8);
+  const int c = (int)(o % n8) * 8;
+  if (p >= a.offsets[El]) return;
+  const int w = kGateUp ? 2 * a.Nout : a.Nout;
+  float v[8], u[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) v[q] = u[q] = 0.f;
+  for (int sp = 0; sp < a.ksplit; ++sp) {
+    const float* prow = a.part + ((long long)sp * a.part_rows + p) * w;
+    const f32x4_t g0 = *reinterpret_cast<const f32x4_t*>(prow + c);
+    const f32x4_t g1 = *reinterpret_cast<const f32x4_t*>(prow + c + 4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] += g0[q], v[q + 4] += g1[q];
+    if constexpr (kGateUp) {
+      const f32x4_t u0 = *reinterpret_cast<const f32x4_t*>(prow + a.Nout + c);
+      const f32x4_t u1 = *reinterpret_cast<const f32x4_t*>(prow + a.Nout + c + 4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) u[q] += u0[q], u[q + 4] += u1[q];
+    }
+  }
+  float h[8];
+  const float gate = (!kGateUp && a.topk_w) ? a.topk_w[a.sorted_slot[p]] : 1.0f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) h[q] = kGateUp ? silu_f32(v[q]) * u[q] : v[q] * gate;
+  *reinterpret_cast<u32x4_t*>(a.out + (long long)p * a.Nout + c) =
+      u32x4_t{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]), pack_bf16x2(h[4], h[5]),
+              pack_bf16x2(h[6], h[7])};
 }
 
 // ---- launch plumbing
@@ -1183,8 +1243,9 @@ hipError_t launch_gemm(const GemmArgs& a, long long max_items, hipStream_t st) {
 template <bool kGateUp, int kWBits, int NB, int kD, int kMinBlocks>
 hipError_t launch_stream(const GemmArgs& a, long long max_items, hipStream_t st) {
   using C = StreamCfg<kGateUp, kWBits, NB, kD>;
-  // whole turns of the ring per item, whole items per output row
-  if ((a.K / C::kSliceK) % kD != 0 || a.Nout % (32 * (kGateUp ? NB / 2 : NB)) != 0)
+  // whole turns of the ring per item (and K range), whole items per output row
+  if (a.ksplit < 1 || (a.K / C::kSliceK) % (kD * a.ksplit) != 0 ||
+      a.Nout % (32 * (kGateUp ? NB / 2 : NB)) != 0 || (a.ksplit > 1 && a.part == nullptr))
     return hipErrorInvalidValue;
   long long grid = (long long)num_cu() * kMinBlocks;
   if ((max_items + 1) / 2 < grid) grid = (max_items + 1) / 2;
@@ -1245,6 +1306,33 @@ int tile_bm(const Shape& s) {
 
 size_t max_tiles(const Shape& s, int bm) { return (size_t)((s.S + bm - 1) / bm) + s.El; }
 
+// bf16 decode with very few slots (a handful of touched experts): the
+// wave-streamed gate/up GEMM with each item's K range split in ks parts, so
+// that the items (at most min(E_l, S) touched experts x groups x ks) about
+// fill the 2048 waves of two 4-wave workgroups per CU; 1 (no split: the
+// staged plan) when the unsplit items already fill them.  A function of the
+// shape only, so the workspace size is too.  (Measured on the Qwen3 shape:
+// gate/up 25.9 -> 18.3 us at T = 1, 28.9 -> 24.0 at T = 2, equal at T = 4;
+// the down GEMM split the same way was slower from T = 2 on, so it stays
+// staged.)
+int small_batch_split(const Shape& s, int K, int groups) {
+  if (s.weight != kBF16 || plan_of(s) != Plan::kDecode) return 1;
+  constexpr long long kWaveSlots = 2048;
+  const long long items = std::min<long long>(s.El, s.S) * groups;
+  int best = 1;
+  for (int ks = 2; ks <= 16; ++ks) {
+    if (items * ks > kWaveSlots) break;
+    if ((K / 16) % (8 * ks) == 0) best = ks;  // whole turns of the 8-slice ring
+  }
+  return best;
+}
+
+// bytes of the gate/up GEMM's split partial products
+size_t split_part_bytes(const Shape& s) {
+  const size_t gu = (size_t)small_batch_split(s, s.d, s.F / 32);
+  return gu > 1 ? gu * s.S * 2 * s.F * sizeof(float) : 0;
+}
+
 }  // namespace
 
 bool use_router_gemm(const Shape& s) { return s.act == kBF16 && s.T >= 1024; }
@@ -1281,9 +1369,9 @@ FfnSchedule ffn_schedule_view(const Shape& s, void* ws) {
 }
 
 size_t ffn_ws_bytes(const Shape& s) {
-  // schedule (at the smallest tile) + tile count + h [S][F]
+  // schedule (at the smallest tile) + tile count + h [S][F] + split partials
   return align_up(max_tiles(s, 32) * sizeof(int4)) + align_up(sizeof(int)) +
-         align_up((size_t)s.S * s.F * act_bytes(s));
+         align_up((size_t)s.S * s.F * act_bytes(s)) + align_up(split_part_bytes(s));
 }
 
 hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
@@ -1298,6 +1386,8 @@ hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
   uint16_t* h = reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(ws) +
                                             align_up(max_tiles(s, 32) * sizeof(int4)) +
                                             align_up(sizeof(int)));
+  float* part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(h) +
+                                         align_up((size_t)s.S * s.F * act_bytes(s)));
   const int bm = sv.bm;
   hipError_t e = hipSuccess;
   if (!schedule_ready) {
@@ -1324,6 +1414,9 @@ hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
   gu.ntiles = ntiles;
   gu.K = s.d;
   gu.Nout = s.F;
+  gu.ksplit = 1;
+  gu.part = part;
+  gu.part_rows = (int)s.S;
 
   GemmArgs dn = gu;
   dn.A = h;
@@ -1368,7 +1461,22 @@ hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
         if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
         if (e == hipSuccess) e = launch_gemm<1, 1, 2, 4, false, 8, 64, 4, 2>(dn, mt * dn.n_tiles_n, st);
       } else {
-        e = launch_gemm<1, 1, 2, 4, true, 16, 64, 4, 1>(gu, mt * gu.n_tiles_n, st);
+        // very few slots: the gate/up GEMM wave-streamed with split K ranges,
+        // then the sums and SiLU
+        const int ks_gu = small_batch_split(s, s.d, s.F / 32);
+        if (ks_gu > 1) {
+          gu.n_tiles_n = s.F / 32;
+          gu.ksplit = ks_gu;
+          e = launch_stream<true, 16, 2, 8, 2>(gu, mt * gu.n_tiles_n * ks_gu, st);
+          if (e == hipSuccess) {
+            const long long n = s.S * (s.F / 8);
+            hipLaunchKernelGGL(split_reduce_kernel<true>, dim3((unsigned)((n + 255) / 256)),
+                               dim3(256), 0, st, gu, s.El);
+            e = hipGetLastError();
+          }
+        } else {
+          e = launch_gemm<1, 1, 2, 4, true, 16, 64, 4, 1>(gu, mt * gu.n_tiles_n, st);
+        }
         if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
         if (e == hipSuccess) e = launch_gemm<1, 1, 2, 4, false, 16, 64, 4, 1>(dn, mt * dn.n_tiles_n, st);
       }
