@@ -303,17 +303,6 @@ def test_blocked_weight_layout_decode_shapes(case, monkeypatch):
     assert torch.equal(forward(pr, gb, blocked=True)["out"], blocked["out"])
 
 
-@pytest.mark.parametrize("name", ["decode", "decode_mxfp4"])
-def test_blocked_weight_layout_full_size(name):
-    pr = synth.make_problem(synth.WORKLOADS[name])
-    g = upload(pr)
-    rows = forward(pr, g)
-    blocked = forward(pr, pack(pr, g), blocked=True)
-    if same_plan_when_blocked(pr.wl):
-        assert torch.equal(rows["out"], blocked["out"])
-    check(pr, blocked)
-
-
 @pytest.mark.parametrize("case", ["mxfp4_plan", "mxfp4_decode_plan"])
 def test_mxfp4_spread_scales(case):
     """E8M0 scales moved by up to 2^8 either way per (32-value block, row): a
@@ -487,14 +476,19 @@ def _sample(T, n, seed):
     return np.sort(rng.choice(T, size=min(n, T), replace=False))
 
 
-@pytest.mark.parametrize("T", [1, 2, 4, 16, 64, 256, 1024, 4096])
-def test_batch_sweep_parity(T):
+@pytest.mark.parametrize("layout,T", [("blocked", T) for T in (1, 2, 4, 8, 16, 64, 256, 1024, 4096)]
+                         + [("rows", T) for T in (1, 2, 4, 8, 16, 64)])
+def test_batch_sweep_parity(layout, T):
     """The Qwen3-shaped layer across the batch sizes of the sweep (the decode
     workload's distributions with T tokens): every tile plan from decode to
-    prefill tiles, on a sample of tokens at the larger sizes."""
+    prefill tiles (and the split-K gate/up path of the smallest batches), on
+    a sample of tokens at the larger sizes; blocked weights as the sweep in
+    bench.py runs them, and row-major ones at decode sizes (row-major prefill
+    tiles are covered by the small cases)."""
     wl = synth.WORKLOADS["decode"].replace(name=f"qwen3_sweep_T{T}", T=T, seed=70 + T % 97)
     pr = synth.make_problem(wl)
-    gpu = forward(pr)
+    g = upload(pr)
+    gpu = forward(pr, pack(pr, g), blocked=True) if layout == "blocked" else forward(pr, g)
     check(pr, gpu, tokens=None if T <= 64 else _sample(T, 24, seed=T))
 
 
@@ -502,12 +496,22 @@ def test_batch_sweep_parity(T):
                                            ("dsv3_rank", 48), ("decode_mxfp4", None),
                                            ("prefill_mxfp4", 64)])
 def test_full_size_workloads(name, n_sample):
+    """Each workload at its full size in the configuration bench.py times
+    (weights in the blocked layout), against the oracle; the row-major layout
+    bit for bit where both sum the same K order, else against the oracle too."""
     wl = synth.WORKLOADS[name]
     print(f"generating {wl.name}", flush=True)
     pr = synth.make_problem(wl)
-    gpu = forward(pr)
+    g = upload(pr)
+    gpu = forward(pr, pack(pr, g), blocked=True)
     tokens = None if n_sample is None else _sample(wl.T, n_sample, seed=7)
     ref, err = check(pr, gpu, tokens=tokens)
+    rows = forward(pr, g)
+    if same_plan_when_blocked(wl):
+        for n in rows:
+            assert torch.equal(rows[n], gpu[n]), n
+    else:
+        check(pr, rows, tokens=tokens)
     counts = ref["counts"]
     print(f"[{wl.name}] kept N={int(ref['offsets'][-1])} touched={int((counts > 0).sum())}/"
           f"{wl.num_local} max/mean={counts.max() / max(counts.mean(), 1e-9):.2f}", flush=True)
