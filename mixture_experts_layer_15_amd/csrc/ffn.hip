@@ -186,6 +186,25 @@ __device__ __forceinline__ void lds_dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t
 #endif
 }
 
+// The same with the nontemporal cache policy (gfx950 "nt"): for weights that
+// are streamed once per step and not re-read by other tiles, so they do not
+// displace the lines that are (measured on the Qwen3 decode step: gate/up
+// 137.0 -> 129.4 us, down 71.5 -> 67.2 us; on prefill-sized tiles, whose
+// weight tiles are re-read by several M tiles through L2, 6 % slower, so
+// only the decode plans use it).
+__device__ __forceinline__ void lds_dma16_buf_nt(__amdgpu_buffer_rsrc_t r, uint32_t voffset,
+                                                 uint32_t soffset, unsigned char* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voffset, soffset, 0, 2);
+#else
+  (void)r;
+  (void)voffset;
+  (void)soffset;
+  (void)lds;
+#endif
+}
+
 // One 4-byte buffer -> LDS load per active lane (buffer_load_dword ... lds):
 // lane i's 4 bytes, from voffset + soffset in the buffer, land at lds + 4 i.
 __device__ __forceinline__ void lds_dma4_buf(__amdgpu_buffer_rsrc_t r, uint32_t voffset,
@@ -402,6 +421,8 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
   // rotation is a function of the item only, so results do not depend on the
   // grid.
   constexpr bool kRotK = kGateUp && kWBits == 16 && C::BM <= 64 && !kRouter && !kBlk;
+  // decode-sized tiles: each weight tile is read by one M tile, streamed nontemporal
+  constexpr bool kNtW = C::BM <= 64 && !kRouter;
   int qrot = 0;
   auto set_src = [&](int j, int row0, int row_end, int n0, const int* rows) {
     j = __builtin_amdgcn_readfirstlane(j);
@@ -477,9 +498,14 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
     _Pragma("unroll") for (int i = 0; i < C::kLoadsA; ++i)                                      \
         lds_dma16_buf(rsA, offA[i], (uint32_t)(qq_) * kBK * 2,                                    \
                       sb_ + (wave * C::kLoadsA + i) * 1024);                                    \
-    _Pragma("unroll") for (int i = 0; i < C::kLoadsB; ++i)                                      \
+    _Pragma("unroll") for (int i = 0; i < C::kLoadsB; ++i) {                                    \
+      if constexpr (kNtW)                                                                       \
+        lds_dma16_buf_nt(b_up(i) ? rsB1 : rsB0, offB[i], (uint32_t)(qq_) * bstage,               \
+                         sb_ + C::kStageA + (wave * C::kLoadsB + i) * 1024);                    \
+      else                                                                                      \
         lds_dma16_buf(b_up(i) ? rsB1 : rsB0, offB[i], (uint32_t)(qq_) * bstage,                  \
                       sb_ + C::kStageA + (wave * C::kLoadsB + i) * 1024);                       \
+    }                                                                                           \
     if constexpr (kFP4) {                                                                       \
       _Pragma("unroll") for (int i = 0; i < C::kLoadsS; ++i)                                    \
         if (l < C::kScaleLanes)                                                                 \
@@ -987,7 +1013,7 @@ __global__ __launch_bounds__(kWave* kStreamWaves, kMinBlocks) void stream_gemm_k
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
         wb[e][n] = __builtin_amdgcn_raw_buffer_load_b128(kGateUp && n >= H ? rsW1 : rsW0, voffW[0],
-                                                         sW[n] + (uint32_t)s * unit_step, 0);
+                                                         sW[n] + (uint32_t)s * unit_step, 2);
         sb[e][n] = __builtin_amdgcn_raw_buffer_load_b8(kGateUp && n >= H ? rsS1 : rsS0, voffS,
                                                        sS[n] + (uint32_t)(2 * s) * a.Nout, 0);
       }
@@ -999,7 +1025,7 @@ __global__ __launch_bounds__(kWave* kStreamWaves, kMinBlocks) void stream_gemm_k
 #pragma unroll
       for (int n = 0; n < NB; ++n)
         wb[e][n] = __builtin_amdgcn_raw_buffer_load_b128(kGateUp && n >= H ? rsW1 : rsW0, voffW[q],
-                                                         sW[n] + (uint32_t)(s >> 2) * unit_step, 0);
+                                                         sW[n] + (uint32_t)(s >> 2) * unit_step, 2);
       tb[e][0] = __builtin_amdgcn_raw_buffer_load_b128(rsA, voffA, (uint32_t)s * 32u, 0);
     }
   };
