@@ -168,6 +168,20 @@ def test_workspace_grows_with_the_problem(lib):
     assert big >= 4096 * 2 * 256 * 2
 
 
+def test_workspace_holds_the_split_partials_of_the_smallest_batches(lib):
+    """Qwen3 shape: with one token the bf16 gate/up GEMM splits K (8 ranges:
+    the most that keep 8 touched experts x 24 wave items x ranges within the
+    2048 waves, with whole 8-slice ring turns per range), so the scratch holds
+    8 x T*k x 2F float32 partial products more than with FP8 weights (same
+    activations, no split); from 64 tokens on there is no split."""
+    def ws(T, weight):
+        return B.moe_workspace_size(B.problem(T, 2048, 128, 8, 768, 0, 128, "bf16", weight),
+                                    B.MOE_CALL_FORWARD)
+    S = 1 * 8
+    assert ws(1, "bf16") - ws(1, "fp8") == 8 * S * 2 * 768 * 4
+    assert ws(64, "bf16") == ws(64, "fp8")
+
+
 def test_status_strings(lib):
     for code, name in [(0, "MOE_OK"), (1, "MOE_ERR_INVALID_ARGUMENT"), (2, "MOE_ERR_UNSUPPORTED"),
                        (3, "MOE_ERR_WORKSPACE_TOO_SMALL"), (4, "MOE_ERR_HIP")]:
