@@ -219,12 +219,16 @@ def topk_select(L: np.ndarray, k: int) -> np.ndarray:
 
     Ties between equal logits go to the lower expert index.  Comparisons are
     exact on the values given (the caller passes the float32 logits it wants
-    the decision taken on).  Returns int32 ``[T, k]`` of global expert ids.
+    the decision taken on).  The pages say nothing of non-finite logits; the
+    reading taken (and stated in the library's contract) is that a NaN ranks
+    as -inf, so it ties with -inf and with other NaNs and those ties also go to
+    the lower index.  Returns int32 ``[T, k]`` of global expert ids.
     """
     L = np.asarray(L)
     T, E = L.shape
     if not 1 <= k <= E:
         raise ValueError("k must lie in [1, E]")
+    L = np.where(np.isnan(L), -np.inf, L)
     experts = np.broadcast_to(np.arange(E), L.shape)
     order = np.lexsort((experts, -L), axis=-1)  # last key is primary
     return order[:, :k].astype(np.int32)

@@ -6,6 +6,7 @@ Expert weight bytes follow "Expert Parallelism for MoE Models" (apxml),
 section "Memory Sizing Equations for MoE Models": experts x parameters per
 expert x bytes per parameter, three d x F matrices per SwiGLU expert.
 """
+import json
 import os
 import subprocess
 import sys
@@ -29,6 +30,21 @@ def test_expert_bytes_follow_the_memory_equation():
     assert bench.expert_bytes(d, F, "mxfp4", 8) == 8 * 3 * (d * F // 2 + d * F // 32)
     # the DeepSeek-V3 shape's 256 experts in FP8: 3 d F bytes each
     assert bench.expert_bytes(7168, 2048, "fp8", 256, with_scales=False) == 256 * 3 * 7168 * 2048
+
+
+def test_expert_bytes_reproduce_the_pages_memory_example():
+    """The apxml page's worked sizing ("Memory Sizing Equations for MoE
+    Models"): 8 experts of 6e9 parameters at 2 bytes are 96 GB, 12 GB per GPU
+    over 8 GPUs, and 6 GB per GPU at 1 byte.  A SwiGLU expert holds 3 d F
+    parameters; d = 50000, F = 40000 gives the page's 6e9."""
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "pages_figures.json")))["expert_memory"]
+    d, F = 50000, 40000
+    assert 3 * d * F == g["params_per_expert"]
+    n = g["n_experts"]
+    assert bench.expert_bytes(d, F, "bf16", n) == g["expert_memory_GB_16bit"] * 1e9
+    assert bench.expert_bytes(d, F, "bf16", n) / g["gpus"] == g["per_gpu_GB_16bit"] * 1e9
+    assert bench.expert_bytes(d, F, "fp8", n, with_scales=False) / g["gpus"] == \
+        g["per_gpu_GB_8bit"] * 1e9
 
 
 def test_algorithmic_counts_on_a_hand_example():

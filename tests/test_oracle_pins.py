@@ -8,6 +8,7 @@ transposed operand) fails at least one of them.
 """
 import itertools
 import json
+import math
 import os
 
 import numpy as np
@@ -86,6 +87,94 @@ def test_dequant_random_codes_match_torch_scaled_decode():
     assert np.array_equal(got[128:], dec[128:] * np.float64(np.float32(3.0)))
 
 
+# ---------------------------------------------------------------- router logits
+#
+# The gate ("Wide Expert Parallelism", section "What is an MoE layer?") scores
+# every expert for a token; the skewed workloads add a per-expert bias to those
+# scores, which moves both the choice and the gate values.  Two pins of
+# ``router_logits``: torch's own affine map in float64 (a different routine),
+# on a problem with T == E so that a bias added along the token axis would
+# broadcast silently instead of raising; and a hand-worked example whose bias
+# changes the chosen experts of one token and the gate values of another.
+
+
+def _pin_router_against_torch_linear(fn):
+    rng = np.random.default_rng(11)
+    T = E = 12
+    d = 20
+    x = rng.standard_normal((T, d))
+    w = rng.standard_normal((d, E))
+    b = rng.standard_normal(E) * 3.0
+    ref = Fnn.linear(torch.from_numpy(x), torch.from_numpy(np.ascontiguousarray(w.T)),
+                     torch.from_numpy(b)).numpy()
+    got = np.asarray(fn(x, w, b), dtype=np.float64)
+    assert got.shape == (T, E)
+    assert np.allclose(got, ref, rtol=1e-13, atol=1e-13)
+    # no bias means a zero bias
+    ref0 = Fnn.linear(torch.from_numpy(x), torch.from_numpy(np.ascontiguousarray(w.T))).numpy()
+    assert np.allclose(np.asarray(fn(x, w, None), dtype=np.float64), ref0, rtol=1e-13, atol=1e-13)
+
+
+def _pin_router_hand_example(fn):
+    # d = 2, E = 3: W_r picks the token's first and second feature as the
+    # scores of experts 0 and 1; expert 2 scores 0 before its bias of 2.5.
+    w = np.array([[1.0, 0.0, 0.0],
+                  [0.0, 1.0, 0.0]])
+    b = np.array([0.0, 0.0, 2.5])
+    x = np.array([[1.0, 2.0],     # scores 1, 2, 0 -> with bias 1, 2, 2.5
+                  [3.0, 1.0]])    # scores 3, 1, 0 -> with bias 3, 1, 2.5
+    L = np.asarray(fn(x, w, b), dtype=np.float64)
+    assert np.array_equal(L, [[1.0, 2.0, 2.5], [3.0, 1.0, 2.5]])
+    idx = orc.topk_select(L, 2)
+    gates = orc.renormalised_gates(L, idx)
+    sig = lambda z: 1.0 / (1.0 + math.exp(-z))  # k = 2: the gates are logistic
+    # token 0: the bias lifts expert 2 over expert 0 (unbiased top-2: 1, 0)
+    assert idx[0].tolist() == [2, 1]
+    assert np.allclose(gates[0], [sig(0.5), sig(-0.5)], rtol=0, atol=1e-15)
+    # token 1: expert 2 replaces expert 1, and the gate of expert 0 drops from
+    # sigmoid(3 - 1) to sigmoid(3 - 2.5)
+    assert idx[1].tolist() == [0, 2]
+    assert np.allclose(gates[1], [sig(0.5), sig(-0.5)], rtol=0, atol=1e-15)
+
+
+def test_router_logits_match_torch_linear_with_bias():
+    _pin_router_against_torch_linear(orc.router_logits)
+
+
+def test_router_bias_moves_selection_and_gates_hand_example():
+    _pin_router_hand_example(orc.router_logits)
+
+
+@pytest.mark.parametrize("slip", ["bias dropped", "bias negated", "bias on the token axis",
+                                  "bias added twice", "router matrix transposed"])
+def test_router_pins_catch_planted_slips(slip):
+    """Mistakes planted in a copy of the oracle's logit formula (on the CPU)
+    must fail at least one of the two pins above."""
+    def slipped(x, w, b):
+        b = None if b is None else np.asarray(b, dtype=np.float64)
+        if slip == "router matrix transposed":
+            L = x @ w.T if w.shape[0] == w.shape[1] else (x @ w)[:, ::-1]
+        else:
+            L = x @ w
+        if b is None or slip == "bias dropped":
+            return L
+        if slip == "bias negated":
+            return L - b[None, :]
+        if slip == "bias on the token axis":
+            return L + b[:, None] if L.shape[0] == L.shape[1] else L + b[None, ::-1]
+        if slip == "bias added twice":
+            return L + 2 * b[None, :]
+        return L + b[None, :]
+
+    failed = 0
+    for pin in (_pin_router_against_torch_linear, _pin_router_hand_example):
+        try:
+            pin(slipped)
+        except AssertionError:
+            failed += 1
+    assert failed >= 1, f"planted slip '{slip}' passed every router pin"
+
+
 # ---------------------------------------------------------------- routing
 
 @pytest.mark.parametrize("T,E,k,levels", [(40, 8, 2, 3), (30, 16, 5, 4), (25, 6, 6, 2), (20, 12, 1, 2)])
@@ -118,6 +207,18 @@ def test_topk_max_over_subsets_brute_force():
     for t in range(10):
         best = max(itertools.combinations(range(7), 3), key=lambda c: sum(float(L[t, e]) for e in c))
         assert set(idx[t].tolist()) == set(best)
+
+
+def test_topk_orders_nan_as_minus_inf_hand_example():
+    # The pages are silent on non-finite logits; the contract reads a NaN as
+    # -inf, so NaN and -inf tie below every finite logit (lower index first)
+    # and +inf ranks above them.
+    L = np.array([[np.nan, 1.0, -np.inf, 0.5, np.nan, np.inf],
+                  [np.nan, np.nan, np.nan, np.nan, np.nan, np.nan],
+                  [-np.inf, np.nan, -np.inf, -2.0, np.nan, -1.0]], dtype=np.float32)
+    assert orc.topk_select(L, 6).tolist() == [[5, 1, 3, 0, 2, 4],
+                                              [0, 1, 2, 3, 4, 5],
+                                              [5, 3, 0, 1, 2, 4]]
 
 
 def test_gates_k2_equal_logistic_of_difference():
