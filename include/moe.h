@@ -33,8 +33,13 @@
  * Conventions for every call
  *  - All device arrays are row-major, 16-byte aligned, owned by the caller
  *    and must stay valid until the stream work completes.  The library never
- *    allocates, frees or synchronises; it keeps no state between calls and
- *    is re-entrant.  Scratch memory comes from the caller (moe_workspace_size).
+ *    allocates, frees or synchronises, and keeps no state between calls:
+ *    every call queries the device it launches on, and the only thing it
+ *    remembers is, per kernel and device, that the kernel's LDS-size
+ *    attribute has been set (an idempotent setting recorded in an atomic bit
+ *    set).  Calls are therefore re-entrant and may run concurrently from
+ *    several host threads (on distinct workspaces and outputs).  Scratch
+ *    memory comes from the caller (moe_workspace_size).
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Every call only enqueues kernels on it and returns.
  *  - The environment variable MOE_MI355X_MAX_WORKGROUPS, if set to a positive
@@ -51,9 +56,15 @@
  *    (act, weight) pairs: (F32, F32), (BF16, BF16), (BF16, FP8_E4M3),
  *    (BF16, MXFP4).  Accumulation is float32; intermediate h is rounded to
  *    the activation format.  FP8 block scales are finite, and each is 0 (the
- *    block contributes nothing) or between 2^-100 and 2^100 in magnitude:
- *    the GEMMs fold them in by rescaling a float32 accumulator from one
- *    128-deep K block to the next.  MXFP4 weights are widened exactly to
+ *    block contributes nothing) or between 2^-100 and 2^100 in magnitude.
+ *    The GEMMs fold them in by rescaling a float32 accumulator from one
+ *    128-deep K block to the next (it holds the running sum divided by the
+ *    latest nonzero scale), which bounds the inputs: the nonzero scales that
+ *    one output feature meets along K (one row of the [F/128][d/128] or
+ *    [d/128][F/128] scale grid) lie within a factor of 2^32 of each other,
+ *    and x and the intermediate h are at most 2^64 in magnitude, so that no
+ *    rescaled partial sum can leave the float32 range; outputs beyond the
+ *    bfloat16 range are outside the contract.  MXFP4 weights are widened exactly to
  *    bfloat16 with their scale applied, which holds for scale bytes 0..252
  *    (2^-127 .. 2^125); bytes 253..255 are outside the contract.
  *  - Expert weights are stored "out x in" (the math matrices transposed):
@@ -142,7 +153,11 @@ const char* moe_status_string(moe_status_t s);
  *  logits   [T][E] float32, required: the output L (including the bias)
  *           when w_router != NULL, the input when w_router == NULL.
  *  topk_idx [T][k] int32 output: global expert ids ordered by (-L, e).
- *  topk_w   [T][k] float32 output: renormalised gates (sum to 1 per token).
+ *           A NaN logit ranks as -inf (it ties with -inf and with other
+ *           NaNs, and those ties also go to the lower index), so every row
+ *           yields k distinct ids in [0, E).
+ *  topk_w   [T][k] float32 output: renormalised gates (sum to 1 per token);
+ *           unspecified for a row whose chosen logits are not all finite.
  *  ws, ws_bytes: scratch of moe_workspace_size(p, MOE_CALL_ROUTE) bytes (the
  *           router matrix transposed to [E][d] and K-split partial sums);
  *           may be NULL / 0 when w_router == NULL.
@@ -229,9 +244,13 @@ typedef struct {
 
 #define MOE_FORWARD_EVENTS 7
 
-/* The whole layer: route, permute, expert FFN (gates folded into the down
- * projection's epilogue), combine.  No host synchronisation: the
- * data-dependent sizes (counts, N) never return to the host.
+/* The whole layer ("Expert Parallelism for MoE Models" (apxml), section
+ * "Mechanics of Token Routing and All-to-All Communication": route each token
+ * to its experts, let each expert compute, send the outputs back and sum
+ * them): route, permute, expert FFN (gates folded into the down projection's
+ * epilogue), combine, with the results of the individual calls above.  No
+ * host synchronisation: the data-dependent sizes (counts, N) never return to
+ * the host.
  *  ws / ws_bytes: scratch of at least moe_workspace_size(p, MOE_CALL_FORWARD). */
 moe_status_t moe_forward(const moe_problem_t* p, const moe_forward_args_t* a, void* ws,
                          size_t ws_bytes, void* stream);

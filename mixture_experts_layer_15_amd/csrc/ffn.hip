@@ -35,6 +35,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "moe_device.h"
@@ -1200,46 +1201,55 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(GemmArgs a, int El) {
 }
 
 // ---- launch plumbing
-int g_num_cu = 0;
+// What a launch needs to know about the device and the caller's grid cap,
+// read once per library call (nothing is cached between calls).
+struct LaunchEnv {
+  int num_cu;          // compute units of the current device
+  long long max_wg;    // MOE_MI355X_MAX_WORKGROUPS, or 0 (no cap)
+};
 
 // MOE_MI355X_MAX_WORKGROUPS caps the persistent GEMM grid (rounded up to a
 // multiple of 8).  Results do not depend on it: every output element comes
 // from one tile with a fixed K order.  Tests use it to give each workgroup
 // many items.
-long long max_workgroups() {
-  const char* v = getenv("MOE_MI355X_MAX_WORKGROUPS");
-  return v ? atoll(v) : 0;
+LaunchEnv launch_env() {
+  LaunchEnv env{256, 0};
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+    env.num_cu = n;
+  if (const char* v = getenv("MOE_MI355X_MAX_WORKGROUPS")) env.max_wg = atoll(v);
+  return env;
 }
 
-int num_cu() {
-  if (g_num_cu == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      g_num_cu = n;
-    else
-      g_num_cu = 256;
-  }
-  return g_num_cu;
+// hipFuncSetAttribute for the dynamic LDS size of `kern`, once per device
+// (devices 0..63 remembered in an atomic bit set; the call is idempotent, so
+// two threads that both make it race harmlessly).
+hipError_t set_lds_attr(const void* kern, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return e;
 }
 
 template <int MB, int WM, int NB, int WN, bool kGateUp, int kWBits, int kBK, int kStages,
           int kMinBlocks, bool kRouter, bool kBlk>
-hipError_t launch_gemm_l(const GemmArgs& a, long long max_items, hipStream_t st) {
+hipError_t launch_gemm_l(const GemmArgs& a, long long max_items, const LaunchEnv& env,
+                         hipStream_t st) {
   using C = Cfg<MB, WM, NB, WN, kGateUp, kWBits, kBK, kStages>;
   auto kern =
       grouped_gemm_kernel<MB, WM, NB, WN, kGateUp, kWBits, kBK, kStages, kMinBlocks, kRouter, kBlk>;
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
-  long long grid = (long long)num_cu() * kMinBlocks;
+  static std::atomic<uint64_t> attr_done{0};  // per instantiation: devices already set
+  hipError_t e = set_lds_attr(reinterpret_cast<const void*>(kern), C::kLds, attr_done);
+  if (e != hipSuccess) return e;
+  long long grid = (long long)env.num_cu * kMinBlocks;
   const long long need = (max_items + kNumXcd - 1) / kNumXcd * kNumXcd;
   if (need < grid) grid = need;
-  if (const long long cap = max_workgroups(); cap > 0 && cap < grid) grid = cap;
+  if (env.max_wg > 0 && env.max_wg < grid) grid = env.max_wg;
   grid = (grid + kNumXcd - 1) / kNumXcd * kNumXcd;
   if (grid < kNumXcd) grid = kNumXcd;
   // stages, then the FP8 scales of two items
@@ -1252,30 +1262,32 @@ hipError_t launch_gemm_l(const GemmArgs& a, long long max_items, hipStream_t st)
 // plans with other K steps take row-major weights only)
 template <int MB, int WM, int NB, int WN, bool kGateUp, int kWBits, int kBK, int kStages,
           int kMinBlocks, bool kRouter = false>
-hipError_t launch_gemm(const GemmArgs& a, long long max_items, hipStream_t st) {
+hipError_t launch_gemm(const GemmArgs& a, long long max_items, const LaunchEnv& env,
+                       hipStream_t st) {
   if constexpr (kBK == 64 && !kRouter) {
     if (a.blocked)
       return launch_gemm_l<MB, WM, NB, WN, kGateUp, kWBits, kBK, kStages, kMinBlocks, kRouter,
-                           true>(a, max_items, st);
+                           true>(a, max_items, env, st);
   } else {
     if (a.blocked) return hipErrorInvalidValue;
   }
   return launch_gemm_l<MB, WM, NB, WN, kGateUp, kWBits, kBK, kStages, kMinBlocks, kRouter, false>(
-      a, max_items, st);
+      a, max_items, env, st);
 }
 
 // Wave-streamed decode GEMMs: one item per wave, item pairs spread over
 // kMinBlocks workgroups per CU (never more workgroups than pairs).
 template <bool kGateUp, int kWBits, int NB, int kD, int kMinBlocks>
-hipError_t launch_stream(const GemmArgs& a, long long max_items, hipStream_t st) {
+hipError_t launch_stream(const GemmArgs& a, long long max_items, const LaunchEnv& env,
+                         hipStream_t st) {
   using C = StreamCfg<kGateUp, kWBits, NB, kD>;
   // whole turns of the ring per item (and K range), whole items per output row
   if (a.ksplit < 1 || (a.K / C::kSliceK) % (kD * a.ksplit) != 0 ||
       a.Nout % (32 * (kGateUp ? NB / 2 : NB)) != 0 || (a.ksplit > 1 && a.part == nullptr))
     return hipErrorInvalidValue;
-  long long grid = (long long)num_cu() * kMinBlocks;
+  long long grid = (long long)env.num_cu * kMinBlocks;
   if ((max_items + 1) / 2 < grid) grid = (max_items + 1) / 2;
-  if (const long long cap = max_workgroups(); cap > 0 && cap < grid) grid = cap;
+  if (env.max_wg > 0 && env.max_wg < grid) grid = env.max_wg;
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL((stream_gemm_kernel<kGateUp, kWBits, NB, kD, kMinBlocks>),
                      dim3((unsigned)grid), dim3(kWave * kStreamWaves), 0, st, a);
@@ -1365,6 +1377,7 @@ bool use_router_gemm(const Shape& s) { return s.act == kBF16 && s.T >= 1024; }
 
 hipError_t router_gemm(const Shape& s, const void* x, const void* w_router_t, float* prod,
                        hipStream_t st) {
+  const LaunchEnv env = launch_env();
   GemmArgs a{};
   a.A = static_cast<const uint16_t*>(x);
   a.a_bytes = (uint32_t)((size_t)s.T * s.d * 2);
@@ -1380,9 +1393,9 @@ hipError_t router_gemm(const Shape& s, const void* x, const void* w_router_t, fl
   // once there are enough of them, which halves the router matrix re-reads
   if (s.T >= 16384)
     return launch_gemm<2, 1, 2, 4, false, 16, 64, 4, 1, true>(
-        a, (long long)((s.T + 63) / 64) * a.n_tiles_n, st);
+        a, (long long)((s.T + 63) / 64) * a.n_tiles_n, env, st);
   return launch_gemm<1, 1, 2, 4, false, 16, 64, 4, 1, true>(
-      a, (long long)((s.T + 31) / 32) * a.n_tiles_n, st);
+      a, (long long)((s.T + 31) / 32) * a.n_tiles_n, env, st);
 }
 
 FfnSchedule ffn_schedule_view(const Shape& s, void* ws) {
@@ -1406,6 +1419,7 @@ hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
                       const void* s_down, const float* topk_w, void* y, void* ws,
                       hipStream_t st, bool schedule_ready, hipEvent_t const* ev) {
   if (s.S == 0) return hipSuccess;
+  const LaunchEnv env = launch_env();
   const FfnSchedule sv = ffn_schedule_view(s, ws);
   int4* tiles = sv.tiles;
   int* ntiles = sv.ntiles;
@@ -1466,7 +1480,7 @@ hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
   if (s.weight == kF32) {
     gu.n_tiles_n = (s.F + kF32BN - 1) / kF32BN;
     dn.n_tiles_n = (s.d + kF32BN - 1) / kF32BN;
-    const int grid = 4 * num_cu();
+    const int grid = 4 * env.num_cu;
     hipLaunchKernelGGL(grouped_f32_kernel<true>, dim3(grid), dim3(256), 0, st, gu);
     e = hipGetLastError();
     if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
@@ -1483,9 +1497,9 @@ hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
       gu.n_tiles_n = ntn(s.F, 128);
       dn.n_tiles_n = ntn(s.d, 256);
       if (fp8) {
-        e = launch_gemm<1, 1, 2, 4, true, 8, 64, 4, 2>(gu, mt * gu.n_tiles_n, st);
+        e = launch_gemm<1, 1, 2, 4, true, 8, 64, 4, 2>(gu, mt * gu.n_tiles_n, env, st);
         if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-        if (e == hipSuccess) e = launch_gemm<1, 1, 2, 4, false, 8, 64, 4, 2>(dn, mt * dn.n_tiles_n, st);
+        if (e == hipSuccess) e = launch_gemm<1, 1, 2, 4, false, 8, 64, 4, 2>(dn, mt * dn.n_tiles_n, env, st);
       } else {
         // very few slots: the gate/up GEMM wave-streamed with split K ranges,
         // then the sums and SiLU
@@ -1493,7 +1507,7 @@ hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
         if (ks_gu > 1) {
           gu.n_tiles_n = s.F / 32;
           gu.ksplit = ks_gu;
-          e = launch_stream<true, 16, 2, 8, 2>(gu, mt * gu.n_tiles_n * ks_gu, st);
+          e = launch_stream<true, 16, 2, 8, 2>(gu, mt * gu.n_tiles_n * ks_gu, env, st);
           if (e == hipSuccess) {
             const long long n = s.S * (s.F / 8);
             hipLaunchKernelGGL(split_reduce_kernel<true>, dim3((unsigned)((n + 255) / 256)),
@@ -1501,39 +1515,39 @@ hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
             e = hipGetLastError();
           }
         } else {
-          e = launch_gemm<1, 1, 2, 4, true, 16, 64, 4, 1>(gu, mt * gu.n_tiles_n, st);
+          e = launch_gemm<1, 1, 2, 4, true, 16, 64, 4, 1>(gu, mt * gu.n_tiles_n, env, st);
         }
         if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-        if (e == hipSuccess) e = launch_gemm<1, 1, 2, 4, false, 16, 64, 4, 1>(dn, mt * dn.n_tiles_n, st);
+        if (e == hipSuccess) e = launch_gemm<1, 1, 2, 4, false, 16, 64, 4, 1>(dn, mt * dn.n_tiles_n, env, st);
       }
       break;
     case Plan::kDecode64:
       gu.n_tiles_n = ntn(s.F, 128);
       dn.n_tiles_n = ntn(s.d, 256);
-      e = launch_gemm<2, 1, 2, 4, true, 16, 64, 4, 1>(gu, mt * gu.n_tiles_n, st);
+      e = launch_gemm<2, 1, 2, 4, true, 16, 64, 4, 1>(gu, mt * gu.n_tiles_n, env, st);
       if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-      if (e == hipSuccess) e = launch_gemm<2, 1, 2, 4, false, 16, 64, 4, 1>(dn, mt * dn.n_tiles_n, st);
+      if (e == hipSuccess) e = launch_gemm<2, 1, 2, 4, false, 16, 64, 4, 1>(dn, mt * dn.n_tiles_n, env, st);
       break;
     case Plan::kFp8:
       gu.n_tiles_n = ntn(s.F, 256);
       dn.n_tiles_n = ntn(s.d, 512);
-      e = launch_gemm<4, 1, 2, 8, true, 8, 64, 2, 1>(gu, mt * gu.n_tiles_n, st);
+      e = launch_gemm<4, 1, 2, 8, true, 8, 64, 2, 1>(gu, mt * gu.n_tiles_n, env, st);
       if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-      if (e == hipSuccess) e = launch_gemm<4, 1, 2, 8, false, 8, 64, 2, 1>(dn, mt * dn.n_tiles_n, st);
+      if (e == hipSuccess) e = launch_gemm<4, 1, 2, 8, false, 8, 64, 2, 1>(dn, mt * dn.n_tiles_n, env, st);
       break;
     case Plan::kWide:
       gu.n_tiles_n = ntn(s.F, 256);
       dn.n_tiles_n = ntn(s.d, 512);
-      e = launch_gemm<2, 2, 4, 4, true, 16, 64, 2, 1>(gu, mt * gu.n_tiles_n, st);
+      e = launch_gemm<2, 2, 4, 4, true, 16, 64, 2, 1>(gu, mt * gu.n_tiles_n, env, st);
       if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-      if (e == hipSuccess) e = launch_gemm<2, 2, 4, 4, false, 16, 64, 2, 1>(dn, mt * dn.n_tiles_n, st);
+      if (e == hipSuccess) e = launch_gemm<2, 2, 4, 4, false, 16, 64, 2, 1>(dn, mt * dn.n_tiles_n, env, st);
       break;
     case Plan::kBig:
       gu.n_tiles_n = ntn(s.F, 128);
       dn.n_tiles_n = ntn(s.d, 256);
-      e = launch_gemm<2, 4, 4, 2, true, 16, 64, 2, 1>(gu, mt * gu.n_tiles_n, st);
+      e = launch_gemm<2, 4, 4, 2, true, 16, 64, 2, 1>(gu, mt * gu.n_tiles_n, env, st);
       if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-      if (e == hipSuccess) e = launch_gemm<2, 4, 4, 2, false, 16, 64, 2, 1>(dn, mt * dn.n_tiles_n, st);
+      if (e == hipSuccess) e = launch_gemm<2, 4, 4, 2, false, 16, 64, 2, 1>(dn, mt * dn.n_tiles_n, env, st);
       break;
     case Plan::kDecodeFp4:
       if (s.blocked) {
@@ -1541,9 +1555,9 @@ hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
         // ahead, two workgroups of 4 waves per CU
         gu.n_tiles_n = s.F / 64;
         dn.n_tiles_n = s.d / 128;
-        e = launch_stream<true, 4, 4, 2, 2>(gu, mt * gu.n_tiles_n, st);
+        e = launch_stream<true, 4, 4, 2, 2>(gu, mt * gu.n_tiles_n, env, st);
         if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-        if (e == hipSuccess) e = launch_stream<false, 4, 4, 2, 2>(dn, mt * dn.n_tiles_n, st);
+        if (e == hipSuccess) e = launch_stream<false, 4, 4, 2, 2>(dn, mt * dn.n_tiles_n, env, st);
       } else {
         // row-major weights: staged 32 x 256 tiles, 128-deep K steps, two
         // stages, three workgroups per CU (streamed, a lane's 16-byte load
@@ -1551,17 +1565,17 @@ hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
         // gate/up)
         gu.n_tiles_n = ntn(s.F, 128);
         dn.n_tiles_n = ntn(s.d, 256);
-        e = launch_gemm<1, 1, 2, 4, true, 4, 128, 2, 3>(gu, mt * gu.n_tiles_n, st);
+        e = launch_gemm<1, 1, 2, 4, true, 4, 128, 2, 3>(gu, mt * gu.n_tiles_n, env, st);
         if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-        if (e == hipSuccess) e = launch_gemm<1, 1, 2, 4, false, 4, 128, 2, 3>(dn, mt * dn.n_tiles_n, st);
+        if (e == hipSuccess) e = launch_gemm<1, 1, 2, 4, false, 4, 128, 2, 3>(dn, mt * dn.n_tiles_n, env, st);
       }
       break;
     case Plan::kFp4:
       gu.n_tiles_n = ntn(s.F, 256);
       dn.n_tiles_n = ntn(s.d, 512);
-      e = launch_gemm<4, 1, 2, 8, true, 4, 64, 4, 1>(gu, mt * gu.n_tiles_n, st);
+      e = launch_gemm<4, 1, 2, 8, true, 4, 64, 4, 1>(gu, mt * gu.n_tiles_n, env, st);
       if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-      if (e == hipSuccess) e = launch_gemm<4, 1, 2, 8, false, 4, 64, 4, 1>(dn, mt * dn.n_tiles_n, st);
+      if (e == hipSuccess) e = launch_gemm<4, 1, 2, 8, false, 4, 64, 4, 1>(dn, mt * dn.n_tiles_n, env, st);
       break;
     case Plan::kF32:
       break;
