@@ -255,6 +255,30 @@ typedef struct {
 moe_status_t moe_forward(const moe_problem_t* p, const moe_forward_args_t* a, void* ws,
                          size_t ws_bytes, void* stream);
 
+/* ---- The whole layer without caller scratch ----
+ *
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * moe_forward with its scratch in a device array that the library holds,
+ * MOE_NOALLOC_SCRATCH_BYTES bytes on every GPU it runs on, from the first
+ * call on that GPU until the process ends.  Same arguments, kernels and
+ * results as moe_forward; the caller still passes every input and output.
+ * Nothing is allocated or freed by the call.
+ *  - Problems whose moe_workspace_size(p, MOE_CALL_FORWARD) exceeds
+ *    MOE_NOALLOC_SCRATCH_BYTES return MOE_ERR_UNSUPPORTED (64 MiB holds, for
+ *    instance, the Qwen3-30B-A3B shape up to about 1300 tokens); invalid
+ *    problems return moe_forward's status.
+ *  - All calls on one GPU share that GPU's array, which keeps the last call's
+ *    contents (no call relies on them): calls that overlap in time on one
+ *    GPU, from several streams or host threads, race on it and must be
+ *    serialised by the caller (one stream does that).
+ *  - The first call on a GPU looks the array's device address up (a HIP
+ *    runtime query, no allocation); a failure there returns MOE_ERR_HIP. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+moe_status_t moe_forward_noalloc(const moe_problem_t* p, const moe_forward_args_t* a,
+                                 void* stream);
+
 /* ---- Expert-parallel load balancing (EPLB) ----
  *
  * "Serving MoE models with expert parallelism on 8xH200" (reviosa), section

@@ -21,6 +21,7 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4 = range(4)
 MOE_CALL_PERMUTE, MOE_CALL_EXPERT_FFN, MOE_CALL_FORWARD, MOE_CALL_ROUTE = range(4)
 MOE_FORWARD_EVENTS = 7
 MOE_LAYOUT_ROWS, MOE_LAYOUT_BLOCKED = range(2)
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20   # include/moe.h
 
 FMT = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3, "mxfp4": MOE_MXFP4}
 
@@ -67,13 +68,14 @@ def load_library() -> ctypes.CDLL:
     lib.moe_expert_ffn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_combine.argtypes = [P, vp, vp, vp, vp, vp]
     lib.moe_forward.argtypes = [P, ctypes.POINTER(ForwardArgs), vp, sz, vp]
+    lib.moe_forward_noalloc.argtypes = [P, ctypes.POINTER(ForwardArgs), vp]
     i64p, i32p, f64p = (ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32),
                         ctypes.POINTER(ctypes.c_double))
     lib.moe_eplb_plan.argtypes = [i64p, i32, i32, i32, i32p, i32p, i32p, f64p]
     lib.moe_eplb_remap.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
     lib.moe_pack_weights.argtypes = [P, i32, vp, vp, vp]
     for f in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
-              "moe_eplb_plan", "moe_eplb_remap", "moe_pack_weights"):
+              "moe_forward_noalloc", "moe_eplb_plan", "moe_eplb_remap", "moe_pack_weights"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -156,14 +158,32 @@ def moe_forward(p, *, x, w_router, router_bias, w_gate, w_up, w_down, out, ws,
                 counts=None, offsets=None, sorted_slot=None, slot_pos=None, events=None,
                 stream=None) -> None:
     """``events``: None, or a ctypes array of MOE_FORWARD_EVENTS hipEvent_t handles."""
-    a = ForwardArgs(_ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w_gate), _ptr(w_up),
-                    _ptr(w_down), _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(out), _ptr(logits),
-                    _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(sorted_slot),
-                    _ptr(slot_pos), None if events is None else ctypes.addressof(events))
+    a = _forward_args(x, w_router, router_bias, w_gate, w_up, w_down, out, s_gate, s_up, s_down,
+                      logits, topk_idx, topk_w, counts, offsets, sorted_slot, slot_pos, events)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     st = load_library().moe_forward(ctypes.byref(p), ctypes.byref(a), _ptr(ws), nbytes,
                                     _stream(stream))
     _check("moe_forward", st)
+
+
+def _forward_args(x, w_router, router_bias, w_gate, w_up, w_down, out, s_gate, s_up, s_down,
+                  logits, topk_idx, topk_w, counts, offsets, sorted_slot, slot_pos, events):
+    return ForwardArgs(_ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w_gate), _ptr(w_up),
+                       _ptr(w_down), _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(out),
+                       _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(offsets),
+                       _ptr(sorted_slot), _ptr(slot_pos),
+                       None if events is None else ctypes.addressof(events))
+
+
+def moe_forward_noalloc(p, *, x, w_router, router_bias, w_gate, w_up, w_down, out,
+                        s_gate=None, s_up=None, s_down=None, logits=None, topk_idx=None,
+                        topk_w=None, counts=None, offsets=None, sorted_slot=None, slot_pos=None,
+                        events=None, stream=None) -> None:
+    """moe_forward with the library's own scratch array (no workspace argument)."""
+    a = _forward_args(x, w_router, router_bias, w_gate, w_up, w_down, out, s_gate, s_up, s_down,
+                      logits, topk_idx, topk_w, counts, offsets, sorted_slot, slot_pos, events)
+    st = load_library().moe_forward_noalloc(ctypes.byref(p), ctypes.byref(a), _stream(stream))
+    _check("moe_forward_noalloc", st)
 
 
 def moe_eplb_plan(load, G: int, R: int):

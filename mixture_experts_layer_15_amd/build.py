@@ -20,7 +20,8 @@ LIB_NAME = "libmoe_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["moe_api.cpp", "route.hip", "permute.hip", "ffn.hip", "combine.hip", "eplb.hip"]
+SOURCES = ["moe_api.cpp", "route.hip", "permute.hip", "ffn.hip", "combine.hip", "eplb.hip",
+           "noalloc.hip"]
 
 # Packed-FP32 VALU forms stay disabled in device code.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",

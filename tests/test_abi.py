@@ -198,3 +198,25 @@ def test_product_code_never_imports_the_oracle():
     # in bench.py only the cpu_baseline leg may use it
     bench = open(os.path.join(os.path.dirname(pkg), "bench.py")).read()
     assert len(re.findall(r"from oracle import", bench)) <= 1
+
+
+def test_noalloc_scratch_limit_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and (int(m.group(1)) << int(m.group(2))) == B.MOE_NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_rejects_on_the_host(lib):
+    """Invalid problems get moe_forward's status, and problems whose scratch
+    exceeds the library's array get MOE_ERR_UNSUPPORTED, before any device
+    work (no GPU is touched here)."""
+    args = B.ForwardArgs(*([FAKE] * 10 + [None] * 8))
+    bad = _p(k=0)
+    assert lib.moe_forward_noalloc(ctypes.byref(bad), ctypes.byref(args), None) == \
+        B.MOE_ERR_INVALID_ARGUMENT
+    big = _p(T=8192, d=2048, E=128, num_local=128, k=8, F=768)
+    assert B.moe_workspace_size(big, B.MOE_CALL_FORWARD) > B.MOE_NOALLOC_SCRATCH_BYTES
+    assert lib.moe_forward_noalloc(ctypes.byref(big), ctypes.byref(args), None) == \
+        B.MOE_ERR_UNSUPPORTED
+    decode = _p(T=64, d=2048, E=128, num_local=128, k=8, F=768)
+    assert B.moe_workspace_size(decode, B.MOE_CALL_FORWARD) <= B.MOE_NOALLOC_SCRATCH_BYTES
