@@ -848,44 +848,90 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
 #undef MOE_ISSUE_STAGE
 }
 
-// ---- float32 path: plain VALU dot products over the same tile schedule
+// ---- float32 path: LDS-staged tiles on the fp32 matrix cores
+// A tile is 32 token rows of one expert segment x 128 output columns; each of
+// the four waves owns a 32 x 32 block (gate/up: a gate and an up block of the
+// same 32 features).  Per 32-deep K stage the workgroup stages the tile's
+// activation rows (gate/up: gathered through sorted_slot) and weight rows
+// into LDS K-major ([k][row], so the 32 lanes that share a K index read 32
+// consecutive words: no bank conflicts), then each wave runs 16
+// v_mfma_f32_32x32x2_f32 per block (float32 products and sums throughout).
 constexpr int kF32BM = 32;
-constexpr int kF32BN = 64;
+constexpr int kF32BN = 128;
+constexpr int kF32BK = 32;
 
 template <bool kGateUp>
 __global__ __launch_bounds__(256) void grouped_f32_kernel(GemmArgs a) {
+  constexpr int kMats = kGateUp ? 2 : 1;
+  __shared__ float As[kF32BK][kF32BM];
+  __shared__ float Bs[kMats][kF32BK][kF32BN];
   const int n_items = *a.ntiles * a.n_tiles_n;
   const float* A = reinterpret_cast<const float*>(a.A);
   const float* W0 = static_cast<const float*>(a.W0);
   const float* W1 = static_cast<const float*>(a.W1);
   float* out = reinterpret_cast<float*>(a.out);
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int l = lane_id();
+  // staging: thread tid copies float4 chunk (tid % 8) of K of activation row
+  // tid / 8, and of weight rows tid / 8 + 32 i
+  const int sr = tid / 8, sk = (tid % 8) * 4;
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const int g = item / a.n_tiles_n;
-    const int nt = item % a.n_tiles_n;
-    const int4 tile = a.tiles[g];
-    const int j = tile.x, row0 = tile.y;
-    const int row_end = tile.z;
-    for (int o = threadIdx.x; o < kF32BM * kF32BN; o += blockDim.x) {
-      const int r = o / kF32BN, c = o % kF32BN;
-      const int p = row0 + r;
-      const int col = nt * kF32BN + c;
-      if (p >= row_end || col >= a.Nout) continue;
-      const long long arow = kGateUp ? (long long)(a.sorted_slot[p] / a.k) : (long long)p;
-      const float* ar = A + arow * a.K;
-      const float* w0 = W0 + ((long long)j * a.Nout + col) * a.K;
-      if (kGateUp) {
-        const float* w1 = W1 + ((long long)j * a.Nout + col) * a.K;
-        float gs = 0.f, us = 0.f;
-        for (int q = 0; q < a.K; ++q) {
-          gs = fmaf(ar[q], w0[q], gs);
-          us = fmaf(ar[q], w1[q], us);
+    const int4 tile = a.tiles[item / a.n_tiles_n];
+    const int j = tile.x, row0 = tile.y, row_end = tile.z;
+    const int n0 = (item % a.n_tiles_n) * kF32BN;
+    const int p_st = min(row0 + sr, row_end - 1);
+    const long long arow = kGateUp ? (long long)(a.sorted_slot[p_st] / a.k) : (long long)p_st;
+    const float* asrc = A + arow * a.K + sk;
+    f32x16_t acc[kMats];
+#pragma unroll
+    for (int m = 0; m < kMats; ++m) acc[m] = f32x16_t{};
+    for (int k0 = 0; k0 < a.K; k0 += kF32BK) {
+      const f32x4_t av = *reinterpret_cast<const f32x4_t*>(asrc + k0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) As[sk + q][sr] = av[q];
+#pragma unroll
+      for (int m = 0; m < kMats; ++m) {
+        const float* W = m == 0 ? W0 : W1;
+#pragma unroll
+        for (int i = 0; i < kF32BN / 32; ++i) {
+          const int col = min(n0 + sr + 32 * i, a.Nout - 1);
+          const f32x4_t wv = *reinterpret_cast<const f32x4_t*>(
+              W + ((long long)j * a.Nout + col) * a.K + k0 + sk);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) Bs[m][sk + q][sr + 32 * i] = wv[q];
         }
-        out[(long long)p * a.Nout + col] = gs / (1.0f + expf(-gs)) * us;
-      } else {
-        float ys = 0.f;
-        for (int q = 0; q < a.K; ++q) ys = fmaf(ar[q], w0[q], ys);
-        const float gw = a.topk_w ? a.topk_w[a.sorted_slot[p]] : 1.0f;
-        out[(long long)p * a.Nout + col] = ys * gw;
+      }
+      __syncthreads();
+      // v_mfma_f32_32x32x2_f32: lane l gives A[row l % 32][k l / 32] and
+      // B[k l / 32][column l % 32]
+#pragma unroll
+      for (int kk = 0; kk < kF32BK; kk += 2) {
+        const float av2 = As[kk + l / 32][l % 32];
+#pragma unroll
+        for (int m = 0; m < kMats; ++m)
+          acc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(av2, Bs[m][kk + l / 32][wave * 32 + l % 32],
+                                                        acc[m], 0, 0, 0);
+      }
+      __syncthreads();
+    }
+    // result block [token row][column]: lane l holds column l % 32, register
+    // r row 8 (r / 4) + 4 (l / 32) + r % 4
+    const int col = n0 + wave * 32 + l % 32;
+    if (col < a.Nout) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int p = row0 + 8 * (r / 4) + 4 * (l / 32) + (r % 4);
+        if (p < row_end) {
+          float v;
+          if constexpr (kGateUp) {
+            const float gs = acc[0][r];
+            v = gs / (1.0f + expf(-gs)) * acc[kMats - 1][r];
+          } else {
+            v = acc[0][r] * (a.topk_w ? a.topk_w[a.sorted_slot[p]] : 1.0f);
+          }
+          out[(long long)p * a.Nout + col] = v;
+        }
       }
     }
   }
