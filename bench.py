@@ -104,11 +104,18 @@ def algorithmic(wl: synth.Workload, counts: np.ndarray, tokens_read: int) -> dic
     gu_flop = 4 * N * d * F
     gu_scales = (2 * (d // 128) * (F // 128) * 4 if wl.weight == "fp8"
                  else 2 * d * F // 32 if wl.weight == "mxfp4" else 0)
-    gu_bytes = int(touched * (2 * d * F * wb + gu_scales) + tokens_read * d * ab + N * F * ab)
+    # the method's bytes: the touched experts' gate and up weights (and
+    # scales) and the token rows read once; the materialised h is the
+    # implementation's traffic, reported beside it
+    gu_bytes = int(touched * (2 * d * F * wb + gu_scales) + tokens_read * d * ab)
+    dn_flop = 2 * N * F * d
+    dn_bytes = int(touched * (d * F * wb + gu_scales // 2))
     return dict(N=N, touched=touched, tokens_read=tokens_read,
                 layer_flop=router_flop + expert_flop, layer_bytes=router_bytes + expert_bytes_,
                 expert_flop=expert_flop, expert_bytes=expert_bytes_,
-                gu_flop=gu_flop, gu_bytes=gu_bytes, gu_unit_bytes=int(2 * d * F * wb + gu_scales))
+                gu_flop=gu_flop, gu_bytes=gu_bytes, gu_bytes_with_h=gu_bytes + N * F * ab,
+                dn_flop=dn_flop, dn_bytes=dn_bytes,
+                gu_unit_bytes=int(2 * d * F * wb + gu_scales))
 
 
 class HipEvents:
@@ -132,31 +139,43 @@ class HipEvents:
         return float(out.value)
 
 
-def measured_traffic(workload: str, kernel: str, layout: str):
-    """HBM bytes per dispatch of the dominant kernel from the committed
-    rocprofv3 FETCH_SIZE/WRITE_SIZE runs (scaled by the copy-kernel
-    calibration), or None when they were taken on other kernel sources or no
-    record covers this workload and kernel."""
+def gemm_sources_sha256() -> str:
+    """Hash of the expert-GEMM sources (the kernels a traffic record covers)."""
     import hashlib
+    m = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        m.update(open(os.path.join(ROOT, f), "rb").read())
+    return m.hexdigest()
+
+
+GEMM_SOURCES = ["mixture_experts_layer_15_amd/csrc/ffn.hip",
+                "mixture_experts_layer_15_amd/csrc/moe_device.h",
+                "mixture_experts_layer_15_amd/csrc/moe_internal.h"]
+
+
+def measured_traffic(workload: str, kernel: str, layout: str):
+    """HBM bytes per dispatch of `kernel` from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE runs (scaled by the copy-kernel calibration), or None
+    when no record covers this workload and kernel or the record was taken on
+    other kernel sources (each record carries the hash of the sources it was
+    measured on)."""
     path = os.path.join(ROOT, "profiles", "gate_up_pmc.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    m = hashlib.sha256()
-    for f in rec["source_files"]:
-        m.update(open(os.path.join(ROOT, f), "rb").read())
-    if m.hexdigest() != rec["source_sha256"]:
-        return None
+    now = gemm_sources_sha256()
     for r in rec["records"]:
-        if (r["workload"] == workload and r["kernel"].startswith(kernel)
-                and r.get("weight_layout", "rows") == layout):
+        if (r["workload"] == workload and r["kernel"] == kernel
+                and r.get("weight_layout", "rows") == layout and r.get("source_sha256") == now):
             return int(r["traffic_bytes_per_dispatch"])
     return None
 
 
-def cpu_baseline(pr: synth.Problem, logits: torch.Tensor, budget_s: float) -> dict:
+def cpu_baseline(pr: synth.Problem, logits: torch.Tensor, budget_s: float,
+                 n_sample: int = 64) -> dict:
     """The float64 oracle, as it stands, on whole steps of the same workload
-    (or on a token sample when one step would exceed the budget)."""
+    (or on a sample of n_sample tokens when one step would exceed the budget;
+    at least one repetition whatever the budget)."""
     from oracle import moe_oracle as orc
     try:
         from threadpoolctl import threadpool_info
@@ -170,7 +189,7 @@ def cpu_baseline(pr: synth.Problem, logits: torch.Tensor, budget_s: float) -> di
     L32 = logits.cpu().numpy()
     rng = np.random.default_rng(0)
     # a sample small enough for ~budget_s of work: whole steps when cheap
-    sample = None if wl.T <= 256 else np.sort(rng.choice(wl.T, size=64, replace=False))
+    sample = None if wl.T <= 256 else np.sort(rng.choice(wl.T, size=n_sample, replace=False))
     n_tok, t0, reps = 0, time.perf_counter(), 0
     while True:
         x64 = orc.decode_act(raw["x"] if sample is None else raw["x"][sample], wl.act)
@@ -185,7 +204,7 @@ def cpu_baseline(pr: synth.Problem, logits: torch.Tensor, budget_s: float) -> di
         if el >= budget_s or reps >= 50:
             break
     what = (f"{reps} whole step(s) of T={wl.T}" if sample is None else
-            f"{reps} x 64 sampled tokens of T={wl.T} (routing of all T each time)")
+            f"{reps} x {n_sample} sampled tokens of T={wl.T} (routing of all T each time)")
     model = ""
     try:
         for line in open("/proc/cpuinfo"):
@@ -201,7 +220,7 @@ def cpu_baseline(pr: synth.Problem, logits: torch.Tensor, budget_s: float) -> di
 
 
 def measure(wl: synth.Workload, steps: int, warmup: int, copies: int, dev,
-            blocked: bool = False) -> dict:
+            blocked: bool = False, warm: bool = True) -> dict:
     """Time `steps` moe_forward calls (after `warmup`) rotating `copies` weight
     copies, then the same steps with the library's stage events, then a warm
     pass on one copy.  Returns times and the routing statistics.  blocked:
@@ -267,21 +286,23 @@ def measure(wl: synth.Workload, steps: int, warmup: int, copies: int, dev,
     share_ev = [l - r for l, r in zip(layer_ev, stage["route"])]  # permute .. combine
 
     # warm: one weight copy, so that the Infinity Cache may serve part of it (info)
-    warm_steps = max(steps // 2, 5)
-    for i in range(3):
-        step(0)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(warm_steps):
-        step(0)
-    torch.cuda.synchronize()
-    warm_ms = (time.perf_counter() - t0) * 1e3 / warm_steps
+    warm_ms = None
+    if warm:
+        warm_steps = max(steps // 2, 5)
+        for i in range(3):
+            step(0)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(warm_steps):
+            step(0)
+        torch.cuda.synchronize()
+        warm_ms = (time.perf_counter() - t0) * 1e3 / warm_steps
 
     sp = slot_pos.cpu().numpy().reshape(wl.T, wl.k)
     tokens_read = int((sp >= 0).any(axis=1).sum())
     return dict(pr=pr, logits=logits, counts=counts.cpu().numpy(), tokens_read=tokens_read,
-                ms_per_step=ms_per_step, stage_ms=stage_ms, layer_ev=layer_ev, share_ev=share_ev,
-                warm_ms=warm_ms, copies=copies)
+                ms_per_step=ms_per_step, stage_ms=stage_ms, stage_ev=stage, layer_ev=layer_ev,
+                share_ev=share_ev, warm_ms=warm_ms, copies=copies)
 
 
 def pct(v, q) -> float:
@@ -438,12 +459,116 @@ def eplb(args, dev) -> None:
         print(json.dumps(line), flush=True)
 
 
+def tile_rows(wl: synth.Workload) -> int:
+    """M-tile height of the library's tile plan for this workload (the rows
+    of one expert's segment that one tile covers)."""
+    S, El = wl.T * wl.k, wl.num_local
+    if wl.weight == "f32":
+        return 32
+    if wl.weight == "mxfp4":
+        return 32 if S <= 64 * El else 128
+    if S <= 16 * El or (S <= 64 * El and wl.weight == "fp8"):
+        return 32
+    if S <= 64 * El:
+        return 64
+    if wl.weight == "fp8":
+        return 128
+    return 256 if S >= 1024 * El else 128
+
+
+def m_padding(wl: synth.Workload, counts: np.ndarray) -> dict:
+    """Rows the expert GEMMs compute beyond the kept slots: every expert
+    segment is cut into M tiles of tile_rows() rows, the last one partly
+    empty.  (The N tiles divide F and d exactly at every workload shape here.)"""
+    bm = tile_rows(wl)
+    c = np.asarray(counts, dtype=np.int64)
+    padded = int((-(-c // bm) * bm).sum())
+    N = int(c.sum())
+    return {"tile_rows": bm, "kept_rows": N, "computed_rows": padded,
+            "padding_frac": round(1.0 - N / padded, 4) if padded else 0.0}
+
+
+def summarize(wl: synth.Workload, m: dict, blocked: bool) -> dict:
+    """Throughput, stage times and roofline fractions of one measured workload.
+
+    Bases, stated with every figure: `ms_per_step_wall` is host wall time over
+    back-to-back steps (no host synchronisation between them); `event_ms` is
+    the spread of the per-step HIP-event brackets moe_forward records on its
+    stream (each step bracketed on its own); kernel figures use the mean of
+    that kernel's event bracket over the timed steps."""
+    cnt = m["counts"]
+    alg = algorithmic(wl, cnt, m["tokens_read"])
+    t_wall = m["ms_per_step"] * 1e-3
+    t_ev = float(np.median(m["layer_ev"])) * 1e-3
+    st = m["stage_ms"]
+
+    def kern(flop, nbytes, ms):
+        t = ms * 1e-3
+        return {"ms": round(ms, 5), "tflops": round(flop / t / 1e12, 2),
+                "frac_mfma_bf16": round(flop / t / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "gbs": round(nbytes / t / 1e9, 1),
+                "frac_hbm": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4),
+                "alg_flop": int(flop), "alg_bytes": int(nbytes)}
+
+    out = {
+        "workload": wl.name, "T": wl.T, "d": wl.d, "E": wl.E, "k": wl.k, "F": wl.F,
+        "local_experts": f"{wl.expert_begin}-{wl.expert_begin + wl.num_local - 1}",
+        "act": wl.act, "weights": wl.weight, "weight_layout": "blocked" if blocked else "rows",
+        "regime": wl.regime, "bias": list(wl.bias) if wl.bias else None,
+        "ms_per_step_wall": round(m["ms_per_step"], 5),
+        "tokens_per_s_wall": round(wl.T / t_wall, 1),
+        "event_ms": {"p10": pct(m["layer_ev"], 10), "p50": pct(m["layer_ev"], 50),
+                     "p90": pct(m["layer_ev"], 90)},
+        "tokens_per_s_event_p50": round(wl.T / t_ev, 1),
+        "kept_slots": alg["N"], "touched_experts": alg["touched"],
+        "tokens_with_local_slot": alg["tokens_read"],
+        "max_over_mean_load": round(float(cnt.max() / max(cnt.mean(), 1e-9)), 2),
+        "m_padding": m_padding(wl, cnt),
+        "stage_ms": {n: round(v, 5) for n, v in st.items()},
+        "gate_up": kern(alg["gu_flop"], alg["gu_bytes"], st["gate_up"]),
+        "down": kern(alg["dn_flop"], alg["dn_bytes"], st["down"]),
+        "layer_wall": kern(alg["layer_flop"], alg["layer_bytes"], m["ms_per_step"]),
+        "layer_event_p50": kern(alg["layer_flop"], alg["layer_bytes"], t_ev * 1e3),
+        "weight_copies": m["copies"],
+    }
+    out["gate_up"]["bytes_with_h"] = alg["gu_bytes_with_h"]
+    out["gate_up"]["kernel"] = gate_up_kernel_name(wl, blocked)
+    if wl.weight == "fp8":
+        out["gate_up"]["frac_mfma_fp8"] = round(alg["gu_flop"] / (st["gate_up"] * 1e-3) / 1e12
+                                                / PEAK_FP8_TFLOPS, 4)
+    if m["warm_ms"] is not None:
+        out["warm_ms_per_step"] = round(m["warm_ms"], 5)
+    if wl.num_local < wl.E:
+        # one expert-parallel rank's share: routing all T tokens over all E
+        # experts is setup shared by the ranks; the share is permute .. combine
+        t_share = float(np.median(m["share_ev"])) * 1e-3
+        out["rank_share"] = {
+            "ms_p50": round(t_share * 1e3, 5), "tokens_per_s": round(wl.T / t_share, 1),
+            "kept_slots_per_s": round(alg["N"] / t_share, 1),
+            "tflops": round(alg["expert_flop"] / t_share / 1e12, 2),
+            "gbs": round(alg["expert_bytes"] / t_share / 1e9, 1),
+            "frac_mfma_bf16": round(alg["expert_flop"] / t_share / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "frac_hbm": round(alg["expert_bytes"] / t_share / 1e9 / PEAK_HBM_GBS, 4)}
+    return out
+
+
+# Workloads measured beside the headline in the default run (each timed with
+# fewer steps: they are compute-bound or large, and the whole command must stay
+# within a few minutes).
+EXTRA_CONFIGS = ["tiny", "decode_mxfp4", "prefill", "prefill_cal", "prefill_mxfp4", "mixtral",
+                 "dsv3_rank", "dsv3_rank_4k"]
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--config", default="decode", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--configs", default=None,
+                    help="comma-separated workloads measured beside the headline one and "
+                         "reported under 'configs' ('none' for none; default: all others when "
+                         "the headline is the decode step)")
     ap.add_argument("--weight-copies", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -481,59 +606,55 @@ def main() -> None:
     copies = args.weight_copies or 4
     blocked = args.layout == "blocked" and wl.weight != "f32"
     m = measure(wl, steps, warmup, copies, dev, blocked)
-    pr, cnt = m["pr"], m["counts"]
-    alg = algorithmic(wl, cnt, m["tokens_read"])
-    ms_per_step, stage_ms = m["ms_per_step"], m["stage_ms"]
-    t_layer = ms_per_step * 1e-3
-    t_gu = stage_ms["gate_up"] * 1e-3
+    pr = m["pr"]
+    sm = summarize(wl, m, blocked)
     decode = wl.regime in ("decode", "tiny")
+    gu = sm["gate_up"]
     if decode:
-        achieved = alg["gu_bytes"] / t_gu / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+        roof = {"bound": "hbm", "achieved": gu["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": gu["frac_hbm"], "traffic": None}
     else:
         peak = PEAK_FP32_TFLOPS if wl.weight == "f32" else PEAK_BF16_TFLOPS
-        achieved = alg["gu_flop"] / t_gu / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
+        roof = {"bound": "mfma", "achieved": gu["tflops"], "peak": peak, "unit": "TFLOP/s",
+                "frac": round(gu["tflops"] / peak, 4), "traffic": None}
         if wl.weight == "fp8":
-            roof["frac_of_fp8_peak"] = round(achieved / PEAK_FP8_TFLOPS, 4)
-    roof["kernel"] = gate_up_kernel_name(wl, blocked)
+            roof["frac_of_fp8_peak"] = gu["frac_mfma_fp8"]
+    roof["kernel"] = gu["kernel"]
     roof["traffic"] = measured_traffic(wl.name, roof["kernel"], "blocked" if blocked else "rows")
-    roof["kernel_ms"] = round(stage_ms["gate_up"], 5)
-    roof["bytes_per_launch"] = alg["gu_bytes"]
-    roof["flop_per_launch"] = alg["gu_flop"]
+    roof["basis"] = ("the gate/up grouped GEMM alone: algorithmic bytes (weights of the touched "
+                     "experts and the token rows, without the materialised h) or FLOPs per "
+                     "launch over the mean of its HIP-event bracket on the library's stream")
+    roof["kernel_ms"] = gu["ms"]
+    roof["bytes_per_launch"] = gu["alg_bytes"]
+    roof["bytes_per_launch_with_h"] = gu["bytes_with_h"]
+    roof["flop_per_launch"] = gu["alg_flop"]
 
-    layer = {"tflops": round(alg["layer_flop"] / t_layer / 1e12, 2),
-             "gbs": round(alg["layer_bytes"] / t_layer / 1e9, 1),
-             "frac_hbm": round(alg["layer_bytes"] / t_layer / 1e9 / PEAK_HBM_GBS, 4),
-             "frac_mfma_bf16": round(alg["layer_flop"] / t_layer / 1e12 / PEAK_BF16_TFLOPS, 4),
-             "kept_slots": alg["N"], "kept_slots_per_s": round(alg["N"] / t_layer, 1),
-             "touched_experts": alg["touched"], "tokens_with_local_slot": alg["tokens_read"],
-             "max_over_mean_load": round(float(cnt.max() / max(cnt.mean(), 1e-9)), 2),
-             "stage_ms": {n: round(v, 5) for n, v in stage_ms.items()},
-             "event_ms_per_step": {"p10": pct(m["layer_ev"], 10), "p50": pct(m["layer_ev"], 50),
-                                   "p90": pct(m["layer_ev"], 90)},
-             "warm_ms_per_step": round(m["warm_ms"], 5)}
-    if wl.num_local < wl.E:
-        # one expert-parallel rank's share: routing all T tokens over all E
-        # experts is setup shared by the ranks; the share is permute .. combine
-        t_share = float(np.median(m["share_ev"])) * 1e-3
-        layer["rank_share"] = {
-            "ms_p50": round(t_share * 1e3, 5), "tokens_per_s": round(wl.T / t_share, 1),
-            "kept_slots_per_s": round(alg["N"] / t_share, 1),
-            "tflops": round(alg["expert_flop"] / t_share / 1e12, 2),
-            "gbs": round(alg["expert_bytes"] / t_share / 1e9, 1),
-            "frac_mfma_bf16": round(alg["expert_flop"] / t_share / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    lw, le = sm["layer_wall"], sm["layer_event_p50"]
+    layer = {"tflops": lw["tflops"], "gbs": lw["gbs"], "frac_hbm": lw["frac_hbm"],
+             "frac_mfma_bf16": lw["frac_mfma_bf16"],
+             "basis": "ms_per_step: host wall time over back-to-back steps",
+             "event_p50": {"ms": le["ms"], "frac_hbm": le["frac_hbm"],
+                           "frac_mfma_bf16": le["frac_mfma_bf16"],
+                           "basis": "median of the per-step HIP-event brackets"},
+             "kept_slots": sm["kept_slots"],
+             "kept_slots_per_s": round(sm["kept_slots"] / (m["ms_per_step"] * 1e-3), 1),
+             "touched_experts": sm["touched_experts"],
+             "tokens_with_local_slot": sm["tokens_with_local_slot"],
+             "max_over_mean_load": sm["max_over_mean_load"], "m_padding": sm["m_padding"],
+             "stage_ms": sm["stage_ms"], "event_ms_per_step": sm["event_ms"],
+             "warm_ms_per_step": sm.get("warm_ms_per_step")}
+    if "rank_share" in sm:
+        layer["rank_share"] = sm["rank_share"]
 
     result = {
         "metric": METRIC,
-        "value": round(wl.T / t_layer, 1),
+        "value": sm["tokens_per_s_wall"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": steps,
         "warmup": warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": sm["ms_per_step_wall"],
+        "ms_per_step_basis": "host wall time over back-to-back steps",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -541,9 +662,8 @@ def main() -> None:
             wl.weight, wl.act),
         "data": "synthetic (seeded; random-init weights of the workload's shape)",
         "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "E": wl.E, "k": wl.k, "F": wl.F,
-                   "local_experts": f"{wl.expert_begin}-{wl.expert_begin + wl.num_local - 1}",
-                   "act": wl.act, "weights": wl.weight, "weight_copies": copies,
-                   "weight_layout": "blocked" if blocked else "rows",
+                   "local_experts": sm["local_experts"], "act": wl.act, "weights": wl.weight,
+                   "weight_copies": copies, "weight_layout": sm["weight_layout"],
                    "parallelism": "single GPU (all experts local)" if wl.num_local == wl.E
                    else "one expert-parallel rank's expert block"},
         "layer": layer,
@@ -552,6 +672,35 @@ def main() -> None:
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(pr, m["logits"], args.cpu_budget)
+    del m, pr
+
+    extra = (EXTRA_CONFIGS if args.config == "decode" else []) if args.configs is None else \
+        [c for c in args.configs.split(",") if c and c != "none"]
+    if extra:
+        cfgs = {}
+        for name in extra:
+            if name == args.config:
+                continue
+            ewl = synth.WORKLOADS[name]
+            dec = ewl.regime in ("decode", "tiny")
+            esteps = min(steps, 20) if dec else min(steps, 10)
+            ewarm = min(warmup, 5) if dec else min(warmup, 3)
+            eblocked = args.layout == "blocked" and ewl.weight != "f32"
+            print(f"[bench] config {name}: generating", file=sys.stderr, flush=True)
+            em = measure(ewl, esteps, ewarm, 4 if dec else 2, dev, eblocked, warm=False)
+            es = summarize(ewl, em, eblocked)
+            es["steps"], es["warmup"] = esteps, ewarm
+            es["gate_up"]["traffic"] = measured_traffic(ewl.name, es["gate_up"]["kernel"],
+                                                        es["weight_layout"])
+            if not args.no_cpu_baseline:
+                es["cpu_baseline"] = cpu_baseline(em["pr"], em["logits"], 2.0, n_sample=16)
+            cfgs[name] = es
+            del em
+            torch.cuda.empty_cache()
+            print(f"[bench] config {name}: {es['ms_per_step_wall']} ms/step, gate/up "
+                  f"{es['gate_up']['frac_mfma_bf16']:.3f} MFMA / {es['gate_up']['frac_hbm']:.3f} "
+                  "HBM", file=sys.stderr, flush=True)
+        result["configs"] = cfgs
     print(json.dumps(result), flush=True)
 
 

@@ -85,6 +85,20 @@ WORKLOADS = {
     "dsv3_rank": Workload("deepseek_v3_ep_rank_T16384_d7168_E256_local0-31_k8_F2048_fp8_zipf1.2",
                           T=16384, d=7168, E=256, k=8, F=2048, expert_begin=0, num_local=32,
                           act="bf16", weight="fp8", bias=("zipf", 1.2, 2.0), seed=5),
+    # Two sensitivity rows, reported beside the gated ones.  The prefill with
+    # the Zipf bias scaled to 1.0 instead of 2.0 (same seed, so the same
+    # tokens and weights): a max/mean expert load of about 4, inside the
+    # "3-5x" the prefill workload's text states, which its own 2.0 recipe
+    # overshoots.  The DeepSeek-V3 rank at T = 4096 without a bias: about 4096
+    # kept slots, the count the rank workload's text states, which its own
+    # T = 16384 recipe exceeds seven times; about 128 rows per expert, so the
+    # expert GEMMs sit near the HBM roofline there.
+    "prefill_cal": Workload("qwen3_30b_a3b_prefill_T8192_d2048_E128_k8_F768_zipf1.1x1.0",
+                            T=8192, d=2048, E=128, k=8, F=768, expert_begin=0, num_local=128,
+                            act="bf16", weight="bf16", bias=("zipf", 1.1, 1.0), seed=3),
+    "dsv3_rank_4k": Workload("deepseek_v3_ep_rank_T4096_d7168_E256_local0-31_k8_F2048_fp8",
+                             T=4096, d=7168, E=256, k=8, F=2048, expert_begin=0, num_local=32,
+                             act="bf16", weight="fp8", seed=8),
 }
 
 

@@ -57,8 +57,12 @@ def test_algorithmic_counts_on_a_hand_example():
     assert a["expert_bytes"] == 4 * 3 * d * F * 2 + 4 * d * 2 + T * d * 2
     assert a["layer_bytes"] == a["expert_bytes"] + d * E * 2
     assert a["gu_flop"] == 4 * 8 * d * F
-    # gate/up: the touched experts' gate and up matrices, the token rows, h written once
-    assert a["gu_bytes"] == 4 * 2 * d * F * 2 + 4 * d * 2 + 8 * F * 2
+    # gate/up: the touched experts' gate and up matrices and the token rows
+    # (the materialised h is reported beside it, not counted)
+    assert a["gu_bytes"] == 4 * 2 * d * F * 2 + 4 * d * 2
+    assert a["gu_bytes_with_h"] == a["gu_bytes"] + 8 * F * 2
+    # down: the touched experts' down matrices
+    assert a["dn_flop"] == 2 * 8 * F * d and a["dn_bytes"] == 4 * d * F * 2
     assert a["gu_unit_bytes"] == 2 * d * F * 2
 
 
