@@ -51,7 +51,7 @@ def gate_up_kernel_name(wl: synth.Workload, blocked: bool = False) -> str:
     tiles up to 16 slots per expert on average, 64-row ones up to 64 (FP8: the
     32-row ones; MXFP4: the wave-streamed kernel on blocked weights, 32-row
     tiles with 128-deep steps on row-major ones), then 128 x 512 tiles for FP8
-    and MXFP4, 256 x 256 from 1024 slots per expert, else 128 x 512)."""
+    and MXFP4, 256 x 256 from 512 slots per expert, else 128 x 512)."""
     S, El = wl.T * wl.k, wl.num_local
     if wl.weight == "f32":
         return "grouped_f32_kernel<true>"
@@ -68,7 +68,7 @@ def gate_up_kernel_name(wl: synth.Workload, blocked: bool = False) -> str:
         args = "2, 1, 2, 4, true, 16, 64, 4, 1"
     elif wl.weight == "fp8":
         args = "4, 1, 2, 8, true, 8, 64, 2, 1"
-    elif S >= 1024 * El:
+    elif S >= 512 * El:
         args = "2, 4, 4, 2, true, 16, 64, 2, 1"
     else:
         args = "2, 2, 4, 4, true, 16, 64, 2, 1"
@@ -473,7 +473,7 @@ def tile_rows(wl: synth.Workload) -> int:
         return 64
     if wl.weight == "fp8":
         return 128
-    return 256 if S >= 1024 * El else 128
+    return 256 if S >= 512 * El else 128
 
 
 def m_padding(wl: synth.Workload, counts: np.ndarray) -> dict:

@@ -1345,8 +1345,12 @@ hipError_t launch_stream(const GemmArgs& a, long long max_items, const LaunchEnv
 // per expert on average (bf16), 64 x 256 tiles, so that an expert's weights
 // are streamed by one M tile instead of two or three.  bf16 prefill: eight
 // waves of 64 x 128, 64-deep K steps and 2 stages, as 128 x 512 tiles when
-// experts hold a few hundred rows (less M padding) or 256 x 256 when they hold
-// a thousand or more (fewer bytes staged per MFMA).  (64-deep steps read whole
+// experts hold a few hundred rows (less M padding) or 256 x 256 from 512 rows
+// per expert on average (fewer bytes staged per MFMA: the tile's loads come
+// through each compute unit's L1 at a rate set by the L1's misses in flight
+// and their latency, so bytes per MFMA decide; the Qwen3 prefill, 512 rows per
+// expert, runs 4 % faster on 256 x 256 than on 128 x 512 despite 15 % M
+// padding against 12 %).  (64-deep steps read whole
 // 128-byte lines of every row per stage and halve the barriers: 9-14 % faster
 // than 32-deep steps with 4 stages.)  FP8 weights: 128 x 512 tiles of eight
 // waves side by side along N (128 x 64 each, so that each weight block is
@@ -1369,7 +1373,7 @@ Plan plan_of(const Shape& s) {
   if (s.S <= 16LL * s.El) return Plan::kDecode;
   if (s.S <= 64LL * s.El) return s.weight == kFP8 ? Plan::kDecode : Plan::kDecode64;
   if (s.weight == kFP8) return Plan::kFp8;
-  return s.S >= 1024LL * s.El ? Plan::kBig : Plan::kWide;
+  return s.S >= 512LL * s.El ? Plan::kBig : Plan::kWide;
 }
 
 bool use_decode_tiles(const Shape& s) {

@@ -71,7 +71,7 @@ def test_roofline_kernel_names_follow_the_tile_plans():
     assert bench.gate_up_kernel_name(w["decode"], True) == \
         "grouped_gemm_kernel<1, 1, 2, 4, true, 16, 64, 4, 1, false, true>"
     assert bench.gate_up_kernel_name(w["decode"], False).endswith(", false, false>")
-    assert bench.gate_up_kernel_name(w["prefill"], True).startswith("grouped_gemm_kernel<2, 2, 4, 4,")
+    assert bench.gate_up_kernel_name(w["prefill"], True).startswith("grouped_gemm_kernel<2, 4, 4, 2,")
     assert bench.gate_up_kernel_name(w["mixtral"], True).startswith("grouped_gemm_kernel<2, 4, 4, 2,")
     assert bench.gate_up_kernel_name(w["dsv3_rank"], True).startswith("grouped_gemm_kernel<4, 1, 2, 8, true, 8,")
     assert bench.gate_up_kernel_name(w["decode_mxfp4"], True) == "stream_gemm_kernel<true, 4, 4, 2, 2>"
