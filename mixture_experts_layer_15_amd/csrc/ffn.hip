@@ -1268,20 +1268,6 @@ LaunchEnv launch_env() {
   return env;
 }
 
-// hipFuncSetAttribute for the dynamic LDS size of `kern`, once per device
-// (devices 0..63 remembered in an atomic bit set; the call is idempotent, so
-// two threads that both make it race harmlessly).
-hipError_t set_lds_attr(const void* kern, int bytes, std::atomic<uint64_t>& done) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
-  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
-  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
-  return e;
-}
-
 template <int MB, int WM, int NB, int WN, bool kGateUp, int kWBits, int kBK, int kStages,
           int kMinBlocks, bool kRouter, bool kBlk>
 hipError_t launch_gemm_l(const GemmArgs& a, long long max_items, const LaunchEnv& env,

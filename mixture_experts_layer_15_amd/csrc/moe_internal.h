@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace moe {
 
 enum Fmt : int { kF32 = 0, kBF16 = 1, kFP8 = 2, kFP4 = 3 };
@@ -22,6 +24,20 @@ struct Shape {
 };
 
 inline size_t align_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
+
+// hipFuncSetAttribute for the dynamic LDS size of `kern`, once per device
+// (devices 0..63 remembered in an atomic bit set; the call is idempotent, so
+// two threads that both make it race harmlessly).
+inline hipError_t set_lds_attr(const void* kern, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 inline int act_bytes(const Shape& s) { return s.act == kF32 ? 4 : 2; }
 
 // ---- route.hip
@@ -36,6 +52,7 @@ hipError_t route(const Shape& s, const void* x, const void* w_router, const floa
                  const float* logits_in, float* logits, int32_t* topk_idx, float* topk_w,
                  void* scratch, hipStream_t st);
 bool use_router_gemm(const Shape& s);
+
 // prod [T][E] = x W_r (float32 accumulation) from the router matrix stored [E][d]
 hipError_t router_gemm(const Shape& s, const void* x, const void* w_router_t, float* prod,
                        hipStream_t st);

@@ -20,34 +20,12 @@
 // A decode batch has few slots (T*k <= 8192): then one workgroup of 16 waves
 // runs all three phases in one kernel, and also writes the expert GEMM's tile
 // schedule (the M tiles of every expert segment), saving four launches.
+#include "dispatch_sort.h"
 #include "moe_device.h"
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
-
-// Inclusive prefix sum over the kThreads threads of a workgroup (thread
-// order): a shuffle scan inside each wave, then each wave adds the totals of
-// the waves before it (two barriers instead of one per doubling step).
-// Integer sums, so the result does not depend on the order of additions.
-// `wave_tot`: LDS scratch of kThreads / 64 elements.
-template <int kThreads, typename V>
-__device__ __forceinline__ V block_inclusive_scan(V v, V* wave_tot) {
-  const int l = lane_id();
-  const int w = threadIdx.x / kWave;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const V t = __shfl_up(v, o, kWave);
-    if (l >= o) v += t;
-  }
-  if (l == kWave - 1) wave_tot[w] = v;
-  __syncthreads();
-  V add = 0;
-  for (int q = 0; q < w; ++q) add += wave_tot[q];
-  __syncthreads();  // wave_tot may be reused by the caller
-  return v + add;
-}
-
 
 constexpr int kChunk = kPermuteChunk;   // slots per workgroup
 constexpr int kThreads = 256;
@@ -174,80 +152,14 @@ __global__ __launch_bounds__(kThreads) void permute_scatter_kernel(
 }
 
 constexpr int kSmallThreads = 1024;
-constexpr int kSmallWaves = kSmallThreads / kWave;
 constexpr long long kSmallSlots = 8192;
 
 __global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(
     const int32_t* __restrict__ idx, int S, int e0, int El, int nbits, int32_t* counts,
     int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos, int bm, int4* tiles, int* ntiles) {
-  __shared__ int hist[kMaxExperts];
-  __shared__ int base[kMaxExperts];
-  __shared__ int wave_tot[kSmallWaves];
-  __shared__ int wcnt[kSmallWaves][kMaxExperts];
-  const int tid = threadIdx.x;
-  const int w = tid / kWave;
-  const int l = lane_id();
-  for (int e = tid; e < El; e += kSmallThreads) {
-    hist[e] = 0;
-#pragma unroll
-    for (int q = 0; q < kSmallWaves; ++q) wcnt[q][e] = 0;
-  }
-  __syncthreads();
-  for (int s = tid; s < S; s += kSmallThreads) {
-    const int e = idx[s] - e0;
-    if ((unsigned)e < (unsigned)El) atomicAdd(&hist[e], 1);
-  }
-  __syncthreads();
-  // exclusive scan of the counts (and of the M tiles per expert)
-  const int cnt = tid < El ? hist[tid] : 0;
-  const int nt = (cnt + bm - 1) / bm;
-  // both sums fit 16 bits: at most 8192 slots and 8192 + El tiles
-  const int incl = block_inclusive_scan<kSmallThreads>(cnt | (nt << 16), wave_tot);
-  const int off = (incl & 0xffff) - cnt;
-  const int tfirst = (incl >> 16) - nt;
-  if (tid < El) {
-    counts[tid] = cnt;
-    offsets[tid] = off;
-    base[tid] = off;
-    if (tiles)
-      for (int i = 0; i < nt; ++i) tiles[tfirst + i] = make_int4(tid, off + i * bm, off + cnt, 0);
-  }
-  if (tid == El - 1) {
-    offsets[El] = incl & 0xffff;
-    if (tiles) *ntiles = incl >> 16;
-  }
-  __syncthreads();
-  // stable scatter, 1024 slots per round in slot order
-  const unsigned long long below = (1ull << l) - 1ull;
-  for (int r0 = 0; r0 < S; r0 += kSmallThreads) {
-    const int s = r0 + tid;
-    const bool valid = s < S;
-    const int e = valid ? idx[s] - e0 : -1;
-    const bool keep = valid && (unsigned)e < (unsigned)El;
-    if (valid && !keep) slot_pos[s] = -1;
-    unsigned long long m = __ballot(keep);
-    for (int bit = 0; bit < nbits; ++bit) {
-      const bool on = keep && ((e >> bit) & 1);
-      const unsigned long long v = __ballot(on);
-      m &= on ? v : ~v;
-    }
-    const int rank = __popcll(m & below);
-    const int c = __popcll(m);
-    if (keep && rank == 0) wcnt[w][e] = c;
-    __syncthreads();
-    if (keep) {
-      int pos = base[e] + rank;
-      for (int q = 0; q < w; ++q) pos += wcnt[q][e];
-      sorted_slot[pos] = s;
-      slot_pos[s] = pos;
-    }
-    __syncthreads();
-    if (keep && rank == 0) {
-      atomicAdd(&base[e], c);  // a sum: the result does not depend on order
-      wcnt[w][e] = 0;
-    }
-    __syncthreads();
-  }
+  __shared__ DispatchSortLds<kSmallThreads> sm;
+  dispatch_sort<kSmallThreads>(idx, S, e0, El, nbits, counts, offsets, sorted_slot, slot_pos, bm,
+                               tiles, ntiles, sm);
 }
 
 }  // namespace

@@ -365,6 +365,46 @@ def test_edge_shapes(case):
         assert torch.all(gpu["topk_w"] == 1.0)
 
 
+# Decode-sized batches: 512 experts (top-k keys spread over 8 per lane), an
+# expert count that is not a multiple of 8 (masked router columns), k = 16
+# with a full 64-token batch, d = 128 (fewer K steps than the router's
+# splits would like), an expert-parallel block; and moe_route alone gives the
+# logits and routing of moe_forward bit for bit.
+DECODE_ROUTE = {
+    "E512_T32": synth.WORKLOADS["decode"].replace(name="fused_T32_d256_E512_k8_F128", T=32, d=256,
+                                                  E=512, num_local=512, k=8, F=128, seed=101),
+    "E300_T20": synth.WORKLOADS["prefill"].replace(name="fused_T20_d384_E300_k6_F128_zipf", T=20,
+                                                   d=384, E=300, num_local=300, k=6, F=128,
+                                                   seed=102),
+    "k16_T64": synth.WORKLOADS["decode"].replace(name="fused_T64_d512_E64_k16_F256", T=64, d=512,
+                                                 E=64, num_local=64, k=16, F=256, seed=103),
+    "d128_T33": synth.WORKLOADS["decode"].replace(name="fused_T33_d128_E40_k3_F128", T=33, d=128,
+                                                  E=40, num_local=40, k=3, F=128, seed=104),
+    "rank_T64": synth.WORKLOADS["dsv3_rank"].replace(name="fused_fp8_T64_d512_E96_local32-63_k8_F256",
+                                                     T=64, d=512, E=96, num_local=32,
+                                                     expert_begin=32, k=8, F=256, seed=105),
+}
+
+
+@pytest.mark.parametrize("case", list(DECODE_ROUTE))
+def test_decode_sized_routing_and_standalone_route(case):
+    wl = DECODE_ROUTE[case]
+    pr = synth.make_problem(wl)
+    g = upload(pr)
+    gpu = forward(pr, g)
+    check(pr, gpu)
+    p = _prob(wl)
+    T, E, k = wl.T, wl.E, wl.k
+    logits = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    gw = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    B.moe_route(p, g["x"], g["w_router"], g["bias"], logits, idx, gw,
+                B.workspace(p, B.MOE_CALL_ROUTE, DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(logits.cpu(), gpu["logits"])
+    assert torch.equal(idx.cpu(), gpu["topk_idx"]) and torch.equal(gw.cpu(), gpu["topk_w"])
+
+
 def test_logits_input_mode_with_planted_ties():
     wl = synth.WORKLOADS["decode"].replace(name="ties", T=256, d=256, E=32, num_local=32, k=6,
                                            F=256)
