@@ -1,7 +1,7 @@
 // The dispatch order of a small batch, computed by one workgroup: a stable
 // counting sort of the kept slots by local expert, plus the expert GEMMs'
-// tile schedule.  Shared by the permutation kernel for small batches and the
-// fused router kernel of decode-sized batches.
+// tile schedule, as a device routine any one-workgroup kernel can run (the
+// permutation kernel for small batches does).
 //
 // "Expert Parallelism for MoE Models" (apxml), section "Mechanics of Token
 // Routing and All-to-All Communication": each token is sent to the device
