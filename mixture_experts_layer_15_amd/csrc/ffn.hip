@@ -94,6 +94,57 @@ struct GemmArgs {
   int ksplit;
   float* part;
   int part_rows;
+  // prefill-sized tiles: virtual workers the items are dealt to (the
+  // device's compute units, a multiple of 8, at most kMaxVW; 0: no tail
+  // split) and the float32 partial sums of the split tail items
+  int vw;
+  float* tail;
+};
+
+// ---- Tail split (prefill-sized tiles)
+// The items are dealt to vw virtual workers, one per compute unit: worker v
+// (on XCD v % 8) runs fw = n_items / vw whole items from its XCD's
+// contiguous range.  The rem = n_items % vw items of the last, partial wave
+// would keep rem compute units busy for a whole item while the others idle;
+// instead each is cut along K into s parts (at most vw / rem, each at least
+// kMinPartStages K stages: a part pays an item's pipeline fill and a store of
+// its partial sums), at most one part per worker.  The parts store float32
+// partial sums; tail_reduce_kernel, launched after the GEMM, adds them in
+// part order and runs the epilogue.  The cut depends on n_items, vw and K
+// only, never on the grid, so results do not depend on the grid either.
+constexpr int kMaxVW = 256;
+constexpr int kMinPartStages = 8;
+constexpr int kMaxParts = 16;
+constexpr int kTailTileFloats = 256 * 256;  // accumulators of one prefill tile (BM x BNW)
+
+struct TailPlan {
+  int full;  // items in whole waves (a multiple of vw)
+  int rem;   // items of the partial wave
+  int s;     // parts per tail item (1: tail items run whole)
+};
+
+// align: K stages per part boundary (FP8: 2, whole 128-deep scale blocks)
+__device__ __forceinline__ TailPlan tail_plan(int n_items, int vw, int nK, int align) {
+  TailPlan t{n_items, 0, 1};
+  if (vw < kNumXcd) return t;
+  t.full = n_items / vw * vw;
+  t.rem = n_items - t.full;
+  if (t.rem > 0) {
+    int s = min(vw / t.rem, min(nK / kMinPartStages, nK / align));
+    t.s = max(min(s, kMaxParts), 1);
+  }
+  return t;
+}
+
+// first K stage of part q of s
+__device__ __forceinline__ int part_begin(int q, int s, int nK, int align) {
+  return (q * (nK / align) / s) * align;
+}
+
+// A unit of a workgroup's work: an item, its K stages [k0, k1), and the
+// index of its partial-sum buffer (-1: a whole item, epilogue in place).
+struct Unit {
+  int item, k0, k1, u;
 };
 
 // ---- LDS layout of the pipeline stages
@@ -288,6 +339,72 @@ struct Cfg {
   static_assert(kSteps % 2 == 0, "fragment buffers alternate by step");
 };
 
+// item -> (M tile, first output column).  Grouped order: items run through
+// groups of group_m consecutive M tiles, M fastest inside a group, so the
+// workgroups of an XCD that run at the same time share a few A tiles and a
+// few weight tiles in L2 (instead of one A tile and as many weight tiles as
+// workgroups).
+__device__ __forceinline__ int2 place_item(int item, int group_m, int n_mtiles, int n_tiles_n,
+                                           int cols_per_tile) {
+  const int per_group = group_m * n_tiles_n;
+  const int grp = item / per_group;
+  const int first_m = grp * group_m;
+  const int gsize = min(group_m, n_mtiles - first_m);
+  const int in_grp = item - grp * per_group;
+  return make_int2(first_m + in_grp % gsize, (in_grp / gsize) * cols_per_tile);
+}
+
+// Epilogue of one 32 x 32 result block of a wave.  Each result block is
+// [feature][token] (MFMA 32x32 layout: lane l holds token column l % 32 in
+// its 16 registers); with the weight-row permutation, register q is feature
+// 16 (l / 32) + q of the block, so a lane stores 16 consecutive features of
+// its token row p from column col: two 16-byte stores.  gate/up:
+// silu(v) * up; down: v times the row's gate gw.
+template <bool kGateUp>
+__device__ __forceinline__ void store_block(const GemmArgs& a, const f32x16_t& v,
+                                            const f32x16_t& up, int p, int col, float gw) {
+  if (col < a.Nout) {
+    uint16_t* orow = a.out + (long long)p * a.Nout;
+    float h[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) h[q] = kGateUp ? silu_f32(v[q]) * up[q] : v[q] * gw;
+    *reinterpret_cast<u32x4_t*>(orow + col) =
+        u32x4_t{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]), pack_bf16x2(h[4], h[5]),
+                pack_bf16x2(h[6], h[7])};
+    *reinterpret_cast<u32x4_t*>(orow + col + 8) =
+        u32x4_t{pack_bf16x2(h[8], h[9]), pack_bf16x2(h[10], h[11]), pack_bf16x2(h[12], h[13]),
+                pack_bf16x2(h[14], h[15])};
+  }
+}
+
+// Epilogue of one wave's accumulators: blocks (m, n) of rows c0 + arow_base +
+// 32 m (those before the segment end ce) and columns n0c + 32 (wn kOut + n) +
+// 16 g; gate/up pairs block n with its up block n + NB / 2.
+template <int MB, int NB, bool kGateUp>
+__device__ __forceinline__ void store_tile_rows(const GemmArgs& a, const f32x16_t (&acc)[MB][NB],
+                                                int c0, int ce, int n0c, int arow_base, int wn,
+                                                int g, const float (&gw)[kGateUp ? 1 : MB]) {
+  constexpr int kOut = kGateUp ? NB / 2 : NB;
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    const int p = c0 + arow_base + m * 32;
+    if (p < ce) {
+#pragma unroll
+      for (int n = 0; n < kOut; ++n)
+        store_block<kGateUp>(a, acc[m][n], acc[m][n + (kGateUp ? kOut : 0)], p,
+                             n0c + wn * kOut * 32 + n * 32 + 16 * g, gw[kGateUp ? 0 : m]);
+    }
+  }
+}
+
+// Partial sums of a split tail item: wave w's accumulators as
+// [w][m][n][r][lane] float4 (r: registers 4r .. 4r + 3), so that each store
+// or load instruction of a wave covers 1 KB of consecutive bytes.
+template <int MB, int NB>
+__device__ __forceinline__ f32x4_t* partial_at(float* unit_buf, int wave, int l) {
+  return reinterpret_cast<f32x4_t*>(unit_buf) + wave * (MB * NB * 4 * kWave) + l;
+}
+
 // kRouter: the router products x W_r as one segment of `rows` token rows,
 // A = x read row by row, W0 = the router matrix stored [E][d], float32 output.
 // kBlk: weights in the blocked layout (units of 32 rows x 64 K values, each
@@ -329,21 +446,62 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
   const int xcd = blockIdx.x % kNumXcd;
   const int per_xcd = gridDim.x / kNumXcd;
   const int slot = blockIdx.x / kNumXcd;
+  auto place = [&](int item) -> int2 {
+    return place_item(item, a.group_m, n_mtiles, a.n_tiles_n, kGateUp ? BNW / 2 : BNW);
+  };
+
+  // This workgroup's units, numbered 0 .. n_units - 1.  Without a tail
+  // split the items are cut into eight contiguous ranges, one per XCD, and
+  // workgroup slot j of an XCD runs items j, j + per_xcd, ... of its range.
+  // With one (prefill-sized tiles, tail_plan), the same for the whole waves
+  // of a.vw virtual workers, then the parts of the tail items.
+  constexpr bool kTail = !kRouter && C::BM >= 128;
+  constexpr int kAlign = kFP8 ? 128 / kBK : 1;
+  static_assert(!kTail || C::BM * C::BNW <= kTailTileFloats, "tail partials of one tile");
+  const int vw = kTail && a.vw >= kNumXcd ? a.vw : gridDim.x;
+  const TailPlan tp = kTail ? tail_plan(n_items, vw, nK, kAlign) : TailPlan{n_items, 0, 1};
+  // Virtual worker v sits on XCD x = v % 8 as its slot j = v / 8 of vw / 8.
+  // Whole items: XCD x owns the contiguous range [x, x + 1) * full / 8, and
+  // slot j runs items j, j + vw / 8, ... of it.  Tail units u (part u / rem
+  // of tail item u % rem) are dealt to the XCDs in contiguous runs of
+  // per_x, so that neighbouring tail items (which share A and weight tiles)
+  // run on one XCD: slot j of XCD x runs unit x * per_x + j.  Workgroup b
+  // runs the virtual workers b, b + G, ... (G = gridDim.x, a multiple of 8:
+  // all on b's XCD, slots jb, jb + G / 8, ...).
+  const int fw = tp.full / vw;                       // whole items per virtual worker
+  const int nu = tp.rem * tp.s;                      // tail units (<= vw)
+  const int per_x = (nu + kNumXcd - 1) / kNumXcd;    // tail units per XCD
+  const int jb = (int)blockIdx.x / kNumXcd;          // b's slot; b's XCD is xcd
+  const int gx = (int)gridDim.x / kNumXcd;           // workgroup slots per XCD
+  const int jmax = max(0, min(per_x, nu - xcd * per_x));  // XCD's slots with a tail unit
+  const int nv = jb < vw / kNumXcd ? (vw / kNumXcd - jb + gx - 1) / gx : 0;  // b's workers
+  const int n1 = jb < jmax ? (jmax - jb + gx - 1) / gx : 0;  // ... with a tail unit
   const int it_begin = (int)((long long)n_items * xcd / kNumXcd);
   const int it_end = (int)((long long)n_items * (xcd + 1) / kNumXcd);
-  const int per_group = a.group_m * a.n_tiles_n;
-
-  // item -> (M tile, first output column).  Grouped order: items run through
-  // groups of group_m consecutive M tiles, M fastest inside a group, so the
-  // workgroups of an XCD that run at the same time share a few A tiles and a
-  // few weight tiles in L2 (instead of one A tile and as many weight tiles as
-  // workgroups).
-  auto place = [&](int item) -> int2 {
-    const int grp = item / per_group;
-    const int first_m = grp * a.group_m;
-    const int gsize = min(a.group_m, n_mtiles - first_m);
-    const int in_grp = item - grp * per_group;
-    return make_int2(first_m + in_grp % gsize, (in_grp / gsize) * (kGateUp ? BNW / 2 : BNW));
+  // Without a split (tp.s == 1) the items keep the plain XCD ranges: the
+  // last partial wave then runs next to the items of the same M tiles on each
+  // XCD (measured 2-4 % faster than dealing the tail items out separately).
+  const bool split = kTail && tp.s > 1;
+  const int n_units = split ? n1 * (fw + 1) + (nv - n1) * fw
+                            : max(0, (it_end - it_begin - slot + per_xcd - 1) / per_xcd);
+  auto unit = [&](int k) -> Unit {
+    if (!split) {
+      return Unit{it_begin + slot + k * per_xcd, 0, nK, -1};
+    } else {
+      int vi, r;
+      if (k < n1 * (fw + 1)) {
+        vi = k / (fw + 1), r = k % (fw + 1);
+      } else {
+        const int kk = k - n1 * (fw + 1);
+        vi = n1 + kk / fw, r = kk % fw;
+      }
+      const int j = jb + vi * gx;  // slot of the virtual worker on XCD xcd
+      if (r < fw) return Unit{xcd * (tp.full / kNumXcd) + j + r * (vw / kNumXcd), 0, nK, -1};
+      const int u = xcd * per_x + j;
+      const int t = u % tp.rem, q = u / tp.rem;  // tail unit u: part q of tail item t
+      return Unit{tp.full + t, part_begin(q, tp.s, nK, kAlign),
+                  part_begin(q + 1, tp.s, nK, kAlign), u};
+    }
   };
 
   // Weight rows enter each 32-row MFMA block permuted: block row 8a + 4g + b
@@ -425,9 +583,12 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
   // decode-sized tiles: each weight tile is read by one M tile, streamed nontemporal
   constexpr bool kNtW = C::BM <= 64 && !kRouter;
   int qrot = 0;
-  auto set_src = [&](int j, int row0, int row_end, int n0, const int* rows) {
+  // (tail parts: qrot is the part's first K stage, and the part's stages
+  // never reach the wrap-around)
+  auto set_src = [&](int j, int row0, int row_end, int n0, const int* rows, int k0) {
     j = __builtin_amdgcn_readfirstlane(j);
     if constexpr (kRotK) qrot = __builtin_amdgcn_readfirstlane((j * 3 + n0 / 32) % nK);
+    if constexpr (kTail) qrot = __builtin_amdgcn_readfirstlane(k0);
     row0 = __builtin_amdgcn_readfirstlane(row0);
     row_end = __builtin_amdgcn_readfirstlane(row_end);
     const uint32_t arow_bytes = (uint32_t)a.K * 2;
@@ -519,19 +680,20 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
   // weight bytes between consecutive K stages of one row
   constexpr uint32_t bstage = kBlk ? 32u * C::kRowB : (uint32_t)C::kRowB;
 
-  int item = it_begin + slot;
-  if (item >= it_end) return;
+  if (n_units <= 0) return;
+  int kc = 0;  // running unit
+  Unit U = unit(0);
 
   // tiles as (expert, first row, end row) and first output column of the
-  // running item (c), the next (x) and the one after it (y)
+  // running unit (c), the next (x) and the one after it (y)
   int cj, c0, ce, n0c, xj = 0, x0 = 0, xe = 1, n0x = 0;
   {
-    const int2 pl = place(item);
+    const int2 pl = place(U.item);
     const int4 t = tile_at(pl.x, 0);
     cj = t.x, c0 = t.y, ce = t.z, n0c = pl.y;
   }
-  if (item + per_xcd < it_end) {
-    const int2 pl = place(item + per_xcd);
+  if (n_units > 1) {
+    const int2 pl = place(unit(1).item);
     const int4 t = tile_at(pl.x, 0);
     xj = t.x, x0 = t.y, xe = t.z, n0x = pl.y;
   }
@@ -542,10 +704,10 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
   // complete, and the compiler places no wait of its own inside the loop.
   wait_vmcnt<0>();
   if constexpr (kFP8) dma_scales(cj, n0c, 0);  // lands before stage 0 does
-  set_src(cj, c0, ce, n0c, rows_cur);
+  set_src(cj, c0, ce, n0c, rows_cur, U.k0);
 #pragma unroll
   for (int st = 0; st < kStages; ++st)
-    if (st < nK) MOE_ISSUE_STAGE(st, st);
+    if (st < U.k1 - U.k0) MOE_ISSUE_STAGE(st, st);
   // MFMA operand fragments of one K step (tokens: B operand; weights: A
   // operand; FP8 weights as raw codes for a pair of steps, widened at use).
   // K permutation shared by both operands: bf16 weights use chunk 2s + g at
@@ -614,13 +776,15 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
   int parity = 0;  // scale buffer of this item
 
   for (;;) {
-    const int item_n = item + per_xcd;
-    const bool has_next = item_n < it_end;
-    const bool has_nn = item_n + per_xcd < it_end;
+    const bool has_next = kc + 1 < n_units;
+    const bool has_nn = kc + 2 < n_units;
+    const Unit X = has_next ? unit(kc + 1) : U;
+    const int y_item = has_nn ? unit(kc + 2).item : 0;
+    const int nKc = U.k1 - U.k0;  // K stages of this unit
 
     // this item's stage 0 has landed once only its later stages (and younger
     // loads or stores) remain in flight
-    if (nK >= kStages)
+    if (nKc >= kStages)
       wait_vmcnt<(kStages - 1) * C::kLoads>();
     else
       wait_vmcnt<0>();
@@ -639,7 +803,7 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
     // the next item's inputs and the tile of the item after it
     int yj = xj, y0 = x0, ye = xe, n0y = n0x;
     int rows_nxt[kRows];
-    if (has_nn) n0y = place(item_n + per_xcd).y;
+    if (has_nn) n0y = place(y_item).y;
     if (has_next) {
       load_rows(x0, xe, rows_nxt);
       if (has_nn) {
@@ -648,7 +812,7 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
         // wait for it (and for every stage load in flight) right here
         int opaque_zero;
         asm volatile("v_mov_b32 %0, 0" : "=v"(opaque_zero));
-        const int4 t = tile_at(place(item_n + per_xcd).x, opaque_zero);
+        const int4 t = tile_at(place(y_item).x, opaque_zero);
         yj = t.x, y0 = t.y, ye = t.z;
       }
       // the other scale buffer was last read by the previous item
@@ -704,10 +868,10 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
     // occupy the matrix pipe, then refill the freed buffer of stage ks with
     // stage ks + kStages and read stage ks + 1's first fragments while the
     // last step's MFMAs run.
-    for (int ks = 0; ks < nK; ++ks) {
+    for (int ks = 0; ks < nKc; ++ks) {
       if constexpr (kFP8) {
-        if ((ks * kBK) % 128 == 0) {  // entering a 128-deep scale block
-          const int kb = (ks * kBK) / 128;
+        if (((U.k0 + ks) * kBK) % 128 == 0) {  // entering a 128-deep scale block
+          const int kb = ((U.k0 + ks) * kBK) / 128;
           anyz = false;
 #pragma unroll
           for (int n = 0; n < NB; ++n) {
@@ -717,7 +881,7 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
             anyz = anyz || zblk[n];
             if (!zblk[n]) {
               const float sv = __int_as_float(bits);
-              if (kb > 0) {
+              if (ks > 0) {  // not the unit's first block
                 const float ratio = rsc[n] / sv;
 #pragma unroll
                 for (int m = 0; m < MB; ++m) acc[m][n] *= ratio;
@@ -739,17 +903,17 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
           else
             sched_alternate<MB + (kFP4 ? 0 : NB), MB * NB>();
         } else {
-          const bool more = ks + 1 < nK;
+          const bool more = ks + 1 < nKc;
           __builtin_amdgcn_sched_barrier(0);
           wait_lgkmcnt0();  // this wave's reads of stage ks have returned
           if (more) {
-            if (ks + kStages - 1 < nK)
+            if (ks + kStages - 1 < nKc)
               wait_vmcnt<(kStages - 2) * C::kLoads>();  // stage ks + 1 landed
             else
               wait_vmcnt<0>();
           }
           stage_barrier();  // stage ks + 1 visible; nobody reads stage ks any more
-          if (ks + kStages < nK) MOE_ISSUE_STAGE(ks + kStages, base + ks + kStages);
+          if (ks + kStages < nKc) MOE_ISSUE_STAGE(ks + kStages, base + ks + kStages);
           __builtin_amdgcn_sched_barrier(0);
           if (more) read_frags(base + ks + 1, 0, 0);
           mfma_step(s, s & 1, (base + ks) & 1);
@@ -771,19 +935,30 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
       // buffers (and the other scale buffer).
       wait_vmcnt<0>();
       stage_barrier();
-      set_src(xj, x0, xe, n0x, rows_nxt);
+      set_src(xj, x0, xe, n0x, rows_nxt, X.k0);
 #pragma unroll
       for (int st = 0; st < kStages; ++st)
-        if (st < nK) MOE_ISSUE_STAGE(st, base + nK + st);
+        if (st < X.k1 - X.k0) MOE_ISSUE_STAGE(st, base + nKc + st);
     } else {
       wait_vmcnt<0>();  // the gates: nothing else is in flight any more
     }
 
-    // ---- epilogue.  Each result block is [feature][token] (MFMA 32x32 layout:
-    // lane l holds token column l % 32 in its 16 registers); with the weight-row
-    // permutation, register q is feature 16 (l / 32) + q of the block, so a
-    // lane stores 16 consecutive features of one token row: two 16-byte stores.
-    if constexpr (kRouter) {
+    // ---- epilogue (store_tile_rows; the router's float32 products below)
+    if (kTail && U.u >= 0) {
+      // a part of a split tail item: its float32 partial sums, for
+      // tail_reduce_kernel (stores only: nothing waits for the next unit's
+      // stages here)
+      f32x4_t* dst = partial_at<MB, NB>(a.tail + (size_t)U.u * kTailTileFloats, wave, l);
+#pragma unroll
+      for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int n = 0; n < NB; ++n)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            dst[((m * NB + n) * 4 + r) * kWave] =
+                f32x4_t{acc[m][n][4 * r], acc[m][n][4 * r + 1], acc[m][n][4 * r + 2],
+                        acc[m][n][4 * r + 3]};
+    } else if constexpr (kRouter) {
       // float32 products; 16-byte stores where a run of 16 columns is whole
       // and aligned, else one column at a time (no loads here: a load would
       // wait for the next item's stages already in flight)
@@ -810,35 +985,13 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
         }
       }
     } else {
-#pragma unroll
-    for (int m = 0; m < MB; ++m) {
-      const int p = c0 + arow_base + m * 32;
-      if (p < ce) {
-        uint16_t* orow = a.out + (long long)p * a.Nout;
-#pragma unroll
-        for (int n = 0; n < (kGateUp ? H : NB); ++n) {
-          const int col = n0c + wn * (kGateUp ? H : NB) * 32 + n * 32 + 16 * g;
-          if (col < a.Nout) {
-            float h[16];
-#pragma unroll
-            for (int q = 0; q < 16; ++q)
-              h[q] = kGateUp ? silu_f32(acc[m][n][q]) * acc[m][n + (kGateUp ? H : 0)][q]
-                             : acc[m][n][q] * gw[kGateUp ? 0 : m];
-            *reinterpret_cast<u32x4_t*>(orow + col) =
-                u32x4_t{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]),
-                        pack_bf16x2(h[4], h[5]), pack_bf16x2(h[6], h[7])};
-            *reinterpret_cast<u32x4_t*>(orow + col + 8) =
-                u32x4_t{pack_bf16x2(h[8], h[9]), pack_bf16x2(h[10], h[11]),
-                        pack_bf16x2(h[12], h[13]), pack_bf16x2(h[14], h[15])};
-          }
-        }
-      }
-    }
+      store_tile_rows<MB, NB, kGateUp>(a, acc, c0, ce, n0c, arow_base, wn, g, gw);
     }
 
     if (!has_next) break;
-    item = item_n;
-    base += nK;
+    ++kc;
+    base += nKc;
+    U = X;
     cj = xj, c0 = x0, ce = xe, n0c = n0x;
     xj = yj, x0 = y0, xe = ye, n0x = n0y;
 #pragma unroll
@@ -846,6 +999,72 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
     parity ^= 1;
   }
 #undef MOE_ISSUE_STAGE
+}
+
+// Sums of the split tail items (tail_plan): one wave per output block of a
+// GEMM wave of a tail item (gate/up: the block and its up block), which adds
+// that block's partial sums in part order (a fixed order: the result does
+// not depend on which part finished first), with up to four parts' loads in
+// flight, and runs the GEMM's epilogue on it.  Launched after the GEMM on the
+// same stream, on a small grid whose waves stride over the blocks; does
+// nothing when the GEMM split no item.
+template <int MB, int WM, int NB, int WN, bool kGateUp>
+__global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs a, int nK, int align) {
+  constexpr int kWaves = WM * WN;
+  constexpr int BNW = 32 * NB * WN;
+  constexpr int kOut = kGateUp ? NB / 2 : NB;  // output blocks per (GEMM wave, m)
+  constexpr int kJobs = kWaves * MB * kOut;    // output blocks per tail item
+  constexpr int kB = kGateUp ? 2 : 1;          // partial blocks per output block
+  constexpr int kChunk = 4;                    // parts loaded at a time
+  const int n_mtiles = *a.ntiles;
+  const TailPlan tp = tail_plan(n_mtiles * a.n_tiles_n, a.vw, nK, align);
+  if (tp.s <= 1) return;
+  const int l = lane_id();
+  const int stride = gridDim.x * 4;
+  for (int job = blockIdx.x * 4 + (int)threadIdx.x / kWave; job < tp.rem * kJobs;
+       job += stride) {
+    const int t = job / kJobs, jr = job % kJobs;
+    const int w = jr / (MB * kOut), m = (jr / kOut) % MB, n = jr % kOut;
+    f32x16_t acc[kB];
+    for (int q0 = 0; q0 < tp.s; q0 += kChunk) {
+      f32x4_t buf[kChunk][kB][4];
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i) {
+        if (q0 + i < tp.s) {
+          // part q of tail item t is unit q * rem + t
+          const f32x4_t* src = partial_at<MB, NB>(
+              a.tail + (size_t)((q0 + i) * tp.rem + t) * kTailTileFloats, w, l);
+#pragma unroll
+          for (int b = 0; b < kB; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              buf[i][b][r] = src[((m * NB + n + b * kOut) * 4 + r) * kWave];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i) {
+        if (q0 + i < tp.s) {
+#pragma unroll
+          for (int b = 0; b < kB; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                acc[b][4 * r + e] =
+                    q0 + i == 0 ? buf[i][b][r][e] : acc[b][4 * r + e] + buf[i][b][r][e];
+        }
+      }
+    }
+    const int2 pl =
+        place_item(tp.full + t, a.group_m, n_mtiles, a.n_tiles_n, kGateUp ? BNW / 2 : BNW);
+    const int4 tile = a.tiles[pl.x];
+    const int p = tile.y + (w % WM) * MB * 32 + (l & 31) + m * 32;
+    if (p < tile.z) {
+      const float gw = (!kGateUp && a.topk_w) ? a.topk_w[a.sorted_slot[p]] : 1.0f;
+      store_block<kGateUp>(a, acc[0], acc[kB - 1], p,
+                           pl.y + (w / WM) * kOut * 32 + n * 32 + 16 * (l >> 5), gw);
+    }
+  }
 }
 
 // ---- float32 path: LDS-staged tiles on the fp32 matrix cores
@@ -1307,6 +1526,23 @@ hipError_t launch_gemm(const GemmArgs& a, long long max_items, const LaunchEnv& 
       a, max_items, env, st);
 }
 
+// A prefill-sized GEMM with the tail split (a.vw virtual workers), then the
+// sums of its split tail items.  The grid covers all virtual workers, as the
+// tail parts can outnumber the items.
+template <int MB, int WM, int NB, int WN, bool kGateUp, int kWBits, int kBK, int kStages,
+          int kMinBlocks>
+hipError_t launch_prefill(const GemmArgs& a, long long max_items, const LaunchEnv& env,
+                          hipStream_t st) {
+  hipError_t e = launch_gemm<MB, WM, NB, WN, kGateUp, kWBits, kBK, kStages, kMinBlocks>(
+      a, std::max<long long>(max_items, a.vw), env, st);
+  if (e != hipSuccess || a.vw < kNumXcd) return e;
+  // then the sums of the split tail items: 64 workgroups of 4 waves stride
+  // over the output blocks
+  hipLaunchKernelGGL((tail_reduce_kernel<MB, WM, NB, WN, kGateUp>), dim3(64), dim3(256), 0, st,
+                     a, a.K / kBK, kWBits == 8 ? 128 / kBK : 1);
+  return hipGetLastError();
+}
+
 // Wave-streamed decode GEMMs: one item per wave, item pairs spread over
 // kMinBlocks workgroups per CU (never more workgroups than pairs).
 template <bool kGateUp, int kWBits, int NB, int kD, int kMinBlocks>
@@ -1360,6 +1596,13 @@ Plan plan_of(const Shape& s) {
   if (s.S <= 64LL * s.El) return s.weight == kFP8 ? Plan::kDecode : Plan::kDecode64;
   if (s.weight == kFP8) return Plan::kFp8;
   return s.S >= 512LL * s.El ? Plan::kBig : Plan::kWide;
+}
+
+// prefill-sized tiles (128 or 256 rows): items dealt to virtual workers with
+// the tail split
+bool uses_tail_split(const Shape& s) {
+  const Plan p = plan_of(s);
+  return p == Plan::kWide || p == Plan::kBig || p == Plan::kFp8 || p == Plan::kFp4;
 }
 
 bool use_decode_tiles(const Shape& s) {
@@ -1443,10 +1686,17 @@ FfnSchedule ffn_schedule_view(const Shape& s, void* ws) {
   return v;
 }
 
+// bytes of the tail split's partial sums (at most kMaxVW tail units of one tile)
+size_t tail_part_bytes(const Shape& s) {
+  return uses_tail_split(s) ? (size_t)kMaxVW * kTailTileFloats * sizeof(float) : 0;
+}
+
 size_t ffn_ws_bytes(const Shape& s) {
   // schedule (at the smallest tile) + tile count + h [S][F] + split partials
+  // + tail partials
   return align_up(max_tiles(s, 32) * sizeof(int4)) + align_up(sizeof(int)) +
-         align_up((size_t)s.S * s.F * act_bytes(s)) + align_up(split_part_bytes(s));
+         align_up((size_t)s.S * s.F * act_bytes(s)) + align_up(split_part_bytes(s)) +
+         align_up(tail_part_bytes(s));
 }
 
 hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
@@ -1464,6 +1714,8 @@ hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
                                             align_up(sizeof(int)));
   float* part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(h) +
                                          align_up((size_t)s.S * s.F * act_bytes(s)));
+  float* tail = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(part) +
+                                         align_up(split_part_bytes(s)));
   const int bm = sv.bm;
   hipError_t e = hipSuccess;
   if (!schedule_ready) {
@@ -1493,6 +1745,12 @@ hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
   gu.ksplit = 1;
   gu.part = part;
   gu.part_rows = (int)s.S;
+  // virtual workers of the tail split: the device's compute units (whole
+  // XCDs), so the cut, and the results, depend on the device only
+  gu.vw = uses_tail_split(s) && env.num_cu >= kNumXcd
+              ? std::min(env.num_cu / kNumXcd * kNumXcd, kMaxVW)
+              : 0;
+  gu.tail = tail;
 
   GemmArgs dn = gu;
   dn.A = h;
@@ -1567,23 +1825,23 @@ hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
     case Plan::kFp8:
       gu.n_tiles_n = ntn(s.F, 256);
       dn.n_tiles_n = ntn(s.d, 512);
-      e = launch_gemm<4, 1, 2, 8, true, 8, 64, 2, 1>(gu, mt * gu.n_tiles_n, env, st);
+      e = launch_prefill<4, 1, 2, 8, true, 8, 64, 2, 1>(gu, mt * gu.n_tiles_n, env, st);
       if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-      if (e == hipSuccess) e = launch_gemm<4, 1, 2, 8, false, 8, 64, 2, 1>(dn, mt * dn.n_tiles_n, env, st);
+      if (e == hipSuccess) e = launch_prefill<4, 1, 2, 8, false, 8, 64, 2, 1>(dn, mt * dn.n_tiles_n, env, st);
       break;
     case Plan::kWide:
       gu.n_tiles_n = ntn(s.F, 256);
       dn.n_tiles_n = ntn(s.d, 512);
-      e = launch_gemm<2, 2, 4, 4, true, 16, 64, 2, 1>(gu, mt * gu.n_tiles_n, env, st);
+      e = launch_prefill<2, 2, 4, 4, true, 16, 64, 2, 1>(gu, mt * gu.n_tiles_n, env, st);
       if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-      if (e == hipSuccess) e = launch_gemm<2, 2, 4, 4, false, 16, 64, 2, 1>(dn, mt * dn.n_tiles_n, env, st);
+      if (e == hipSuccess) e = launch_prefill<2, 2, 4, 4, false, 16, 64, 2, 1>(dn, mt * dn.n_tiles_n, env, st);
       break;
     case Plan::kBig:
       gu.n_tiles_n = ntn(s.F, 128);
       dn.n_tiles_n = ntn(s.d, 256);
-      e = launch_gemm<2, 4, 4, 2, true, 16, 64, 2, 1>(gu, mt * gu.n_tiles_n, env, st);
+      e = launch_prefill<2, 4, 4, 2, true, 16, 64, 2, 1>(gu, mt * gu.n_tiles_n, env, st);
       if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-      if (e == hipSuccess) e = launch_gemm<2, 4, 4, 2, false, 16, 64, 2, 1>(dn, mt * dn.n_tiles_n, env, st);
+      if (e == hipSuccess) e = launch_prefill<2, 4, 4, 2, false, 16, 64, 2, 1>(dn, mt * dn.n_tiles_n, env, st);
       break;
     case Plan::kDecodeFp4:
       if (s.blocked) {
@@ -1609,9 +1867,9 @@ hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
     case Plan::kFp4:
       gu.n_tiles_n = ntn(s.F, 256);
       dn.n_tiles_n = ntn(s.d, 512);
-      e = launch_gemm<4, 1, 2, 8, true, 4, 64, 4, 1>(gu, mt * gu.n_tiles_n, env, st);
+      e = launch_prefill<4, 1, 2, 8, true, 4, 64, 4, 1>(gu, mt * gu.n_tiles_n, env, st);
       if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-      if (e == hipSuccess) e = launch_gemm<4, 1, 2, 8, false, 4, 64, 4, 1>(dn, mt * dn.n_tiles_n, env, st);
+      if (e == hipSuccess) e = launch_prefill<4, 1, 2, 8, false, 4, 64, 4, 1>(dn, mt * dn.n_tiles_n, env, st);
       break;
     case Plan::kF32:
       break;

@@ -261,6 +261,52 @@ def test_many_items_per_workgroup(case, monkeypatch):
     check(pr, narrow)
 
 
+# Prefill-sized tiles deal their items to one virtual worker per compute unit
+# and cut each item of the last, partial wave along K into parts, whose
+# float32 partial sums a second kernel adds in part order.  Cases with whole
+# waves and a split tail (gate/up), and with only tail items (down), on each
+# prefill tile plan: (tile rows, gate/up features per N tile, down columns
+# per N tile).
+TAIL = {
+    "wide": (synth.WORKLOADS["prefill"].replace(
+        name="bf16_T1056_d1024_E16_k4_F2048_tail", T=1056, d=1024, E=16, num_local=16, k=4,
+        F=2048, seed=74, bias=()), 128, 256, 512),
+    "big": (synth.WORKLOADS["mixtral"].replace(
+        name="bf16_T4200_d1024_E4_k2_F1024_tail", T=4200, d=1024, E=4, num_local=4, k=2, F=1024,
+        seed=75), 256, 128, 256),
+    "fp8": (synth.WORKLOADS["dsv3_rank"].replace(
+        name="fp8_T4200_d1024_E16_local0-7_k4_F1024_tail", T=4200, d=1024, E=16, num_local=8,
+        expert_begin=0, k=4, F=1024, seed=76), 128, 256, 512),
+}
+
+
+@pytest.mark.parametrize("case", list(TAIL))
+def test_tail_split_items(case, monkeypatch):
+    """The split tail against the oracle (every token), and the same bits with
+    the grid capped at 8 and 24 workgroups (each then runs many virtual
+    workers' items and parts in turn)."""
+    wl, bm, gu_cols, dn_cols = TAIL[case]
+    pr = synth.make_problem(wl)
+    g = upload(pr)
+    full = forward(pr, g)
+    # the case exercises what it is meant to: a split gate/up tail after
+    # whole waves, and a down GEMM with fewer items than compute units
+    vw = torch.cuda.get_device_properties(0).multi_processor_count // 8 * 8
+    mt = int(sum((int(c) + bm - 1) // bm for c in full["counts"].numpy()))
+    gu_items, dn_items = mt * (wl.F // gu_cols), mt * (wl.d // dn_cols)
+    print(f"[{wl.name}] M tiles {mt}, gate/up items {gu_items}, down items {dn_items}, "
+          f"virtual workers {vw}", flush=True)
+    assert gu_items > vw and 0 < gu_items % vw <= vw // 2
+    assert dn_items < vw
+    # (a tail item is cut only where two parts of at least 8 K stages of 64
+    # fit: K = d >= 1024 here)
+    assert wl.d >= 2 * 8 * 64
+    check(pr, full)
+    for cap in ("8", "24"):
+        monkeypatch.setenv("MOE_MI355X_MAX_WORKGROUPS", cap)
+        assert torch.equal(forward(pr, g)["out"], full["out"]), cap
+
+
 @pytest.mark.parametrize("case", ["fp8_plan", "fp8_decode_plan"])
 def test_fp8_zero_and_spread_block_scales(case):
     """Block scales that vary by up to 2^16 along K and blocks whose scale is 0
