@@ -469,7 +469,7 @@ def tile_rows(wl: synth.Workload) -> int:
         return 32 if S <= 64 * El else 128
     if S <= 16 * El or (S <= 64 * El and wl.weight == "fp8"):
         return 32
-    if S <= 64 * El:
+    if S < 64 * El:
         return 64
     if wl.weight == "fp8":
         return 128

@@ -1593,7 +1593,12 @@ Plan plan_of(const Shape& s) {
   if (s.weight == kF32) return Plan::kF32;
   if (s.weight == kFP4) return s.S <= 64LL * s.El ? Plan::kDecodeFp4 : Plan::kFp4;
   if (s.S <= 16LL * s.El) return Plan::kDecode;
-  if (s.S <= 64LL * s.El) return s.weight == kFP8 ? Plan::kDecode : Plan::kDecode64;
+  // bf16: 64-row tiles below 64 slots per expert on average; from 64 on,
+  // about half the experts overflow one 64-row tile and would stream their
+  // weights twice (Qwen3 shape, T = 1024: 0.349 ms against 0.310 on 128-row
+  // tiles; at T = 896, 0.282 against 0.307)
+  if (s.weight == kFP8 && s.S <= 64LL * s.El) return Plan::kDecode;
+  if (s.S < 64LL * s.El) return Plan::kDecode64;
   if (s.weight == kFP8) return Plan::kFp8;
   return s.S >= 512LL * s.El ? Plan::kBig : Plan::kWide;
 }
