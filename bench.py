@@ -683,8 +683,9 @@ def main() -> None:
                 continue
             ewl = synth.WORKLOADS[name]
             dec = ewl.regime in ("decode", "tiny")
-            esteps = min(steps, 20) if dec else min(steps, 10)
-            ewarm = min(warmup, 5) if dec else min(warmup, 3)
+            # fixed, small step counts (a few ms of GPU time each): the
+            # headline's --steps / --warmup do not apply to these lines
+            esteps, ewarm = (40, 10) if dec else (20, 5)
             eblocked = args.layout == "blocked" and ewl.weight != "f32"
             print(f"[bench] config {name}: generating", file=sys.stderr, flush=True)
             em = measure(ewl, esteps, ewarm, 4 if dec else 2, dev, eblocked, warm=False)

@@ -1536,9 +1536,10 @@ hipError_t launch_prefill(const GemmArgs& a, long long max_items, const LaunchEn
   hipError_t e = launch_gemm<MB, WM, NB, WN, kGateUp, kWBits, kBK, kStages, kMinBlocks>(
       a, std::max<long long>(max_items, a.vw), env, st);
   if (e != hipSuccess || a.vw < kNumXcd) return e;
-  // then the sums of the split tail items: 64 workgroups of 4 waves stride
-  // over the output blocks
-  hipLaunchKernelGGL((tail_reduce_kernel<MB, WM, NB, WN, kGateUp>), dim3(64), dim3(256), 0, st,
+  // then the sums of the split tail items: 512 workgroups of 4 waves stride
+  // over the output blocks (Mixtral's down GEMM: 4096 blocks, 31 us on 64
+  // workgroups)
+  hipLaunchKernelGGL((tail_reduce_kernel<MB, WM, NB, WN, kGateUp>), dim3(512), dim3(256), 0, st,
                      a, a.K / kBK, kWBits == 8 ? 128 / kBK : 1);
   return hipGetLastError();
 }
