@@ -305,6 +305,42 @@ def measure(wl: synth.Workload, steps: int, warmup: int, copies: int, dev,
                 share_ev=share_ev, warm_ms=warm_ms, copies=copies)
 
 
+# Dense bf16 GEMMs with the FLOPs of the prefill workloads' expert GEMMs
+# (rows = kept slots, all experts' rows against one weight matrix): what the
+# vendor library reaches on the same shapes without the gather, the ragged
+# expert segments or the SwiGLU epilogue.  (name, rows M, output columns N,
+# reduction K)
+DENSE_REF = [("qwen3_prefill_gate_up", 65536, 1536, 2048), ("qwen3_prefill_down", 65536, 2048, 768),
+             ("mixtral_gate_up", 8192, 28672, 4096), ("mixtral_down", 8192, 4096, 14336),
+             ("dsv3_rank_gate_up", 28535, 4096, 7168), ("dsv3_rank_down", 28535, 7168, 2048)]
+
+
+def dense_ref(args, dev) -> None:
+    """torch.matmul on [M, K] x [K, N] bf16 (both operands contiguous), timed
+    with events on the current stream: one JSON line per GEMM."""
+    g = torch.Generator(device="cpu").manual_seed(0)
+    for name, M, N, K in DENSE_REF:
+        a = torch.randn((M, K), generator=g).to(torch.bfloat16).to(dev)
+        b = (torch.randn((K, N), generator=g) / K ** 0.5).to(torch.bfloat16).to(dev)
+        for _ in range(5):
+            c = torch.matmul(a, b)
+        torch.cuda.synchronize()
+        n = args.steps or 20
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            c = torch.matmul(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / n
+        tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        print(json.dumps({"dense_ref": name, "M": M, "N": N, "K": K, "ms": round(ms, 4),
+                          "tflops": round(tflops, 1), "frac_mfma_bf16": round(tflops / 2500.0, 4),
+                          "library": "torch.matmul (hipBLASLt)"}), flush=True)
+        del a, b, c
+        torch.cuda.empty_cache()
+
+
 def pct(v, q) -> float:
     return round(float(np.percentile(np.asarray(v), q)), 5)
 
@@ -581,6 +617,9 @@ def main() -> None:
     ap.add_argument("--sweep", default=None,
                     help="comma-separated token counts: batch sweep at the Qwen3 shape "
                          "(one JSON line per T instead of the bench line)")
+    ap.add_argument("--dense-ref", action="store_true",
+                    help="reference only: torch.matmul (hipBLASLt) on dense bf16 GEMMs of the "
+                         "prefill workloads' expert-GEMM shapes (one JSON line per GEMM)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the MoE layer: only --gpus 1 is supported "
@@ -596,6 +635,9 @@ def main() -> None:
         return
     if args.eplb:
         eplb(args, dev)
+        return
+    if args.dense_ref:
+        dense_ref(args, dev)
         return
 
     wl = synth.WORKLOADS[args.config]

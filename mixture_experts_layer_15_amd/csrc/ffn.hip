@@ -1535,7 +1535,8 @@ hipError_t launch_prefill(const GemmArgs& a, long long max_items, const LaunchEn
                           hipStream_t st) {
   hipError_t e = launch_gemm<MB, WM, NB, WN, kGateUp, kWBits, kBK, kStages, kMinBlocks>(
       a, std::max<long long>(max_items, a.vw), env, st);
-  if (e != hipSuccess || a.vw < kNumXcd) return e;
+  // (no item can be split when K holds fewer than two parts' worth of stages)
+  if (e != hipSuccess || a.vw < kNumXcd || a.K / kBK < 2 * kMinPartStages) return e;
   // then the sums of the split tail items: 512 workgroups of 4 waves stride
   // over the output blocks (Mixtral's down GEMM: 4096 blocks, 31 us on 64
   // workgroups)
