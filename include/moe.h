@@ -266,8 +266,9 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_forward_args_t* a, vo
  * Nothing is allocated or freed by the call.
  *  - Problems whose moe_workspace_size(p, MOE_CALL_FORWARD) exceeds
  *    MOE_NOALLOC_SCRATCH_BYTES return MOE_ERR_UNSUPPORTED (64 MiB holds, for
- *    instance, the Qwen3-30B-A3B shape up to about 1300 tokens); invalid
- *    problems return moe_forward's status.
+ *    instance, the Qwen3-30B-A3B shape up to 1023 tokens, its decode-sized
+ *    tile plans; from 64 slots per expert the prefill-sized plans add 64 MiB
+ *    of tail partial sums); invalid problems return moe_forward's status.
  *  - All calls on one GPU share that GPU's array, which keeps the last call's
  *    contents (no call relies on them): calls that overlap in time on one
  *    GPU, from several streams or host threads, race on it and must be

@@ -220,3 +220,9 @@ def test_noalloc_rejects_on_the_host(lib):
         B.MOE_ERR_UNSUPPORTED
     decode = _p(T=64, d=2048, E=128, num_local=128, k=8, F=768)
     assert B.moe_workspace_size(decode, B.MOE_CALL_FORWARD) <= B.MOE_NOALLOC_SCRATCH_BYTES
+    # the header's example: the Qwen3 shape fits up to 1023 tokens (decode-sized
+    # tile plans); at 1024 the prefill-sized plans add their tail partial sums
+    last = _p(T=1023, d=2048, E=128, num_local=128, k=8, F=768)
+    first = _p(T=1024, d=2048, E=128, num_local=128, k=8, F=768)
+    assert B.moe_workspace_size(last, B.MOE_CALL_FORWARD) <= B.MOE_NOALLOC_SCRATCH_BYTES
+    assert B.moe_workspace_size(first, B.MOE_CALL_FORWARD) > B.MOE_NOALLOC_SCRATCH_BYTES
