@@ -277,6 +277,9 @@ TAIL = {
     "fp8": (synth.WORKLOADS["dsv3_rank"].replace(
         name="fp8_T4200_d1024_E16_local0-7_k4_F1024_tail", T=4200, d=1024, E=16, num_local=8,
         expert_begin=0, k=4, F=1024, seed=76), 128, 256, 512),
+    "mxfp4": (synth.WORKLOADS["decode_mxfp4"].replace(
+        name="mxfp4_T2100_d1024_E16_k4_F1024_tail", T=2100, d=1024, E=16, num_local=16, k=4,
+        F=1024, seed=77, regime="prefill"), 128, 256, 512),
 }
 
 
