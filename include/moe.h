@@ -44,7 +44,12 @@
  *    Every call only enqueues kernels on it and returns.
  *  - The environment variable MOE_MI355X_MAX_WORKGROUPS, if set to a positive
  *    number, caps the workgroups of the persistent expert GEMM kernels (a
- *    test aid; results are the same for every value).
+ *    test aid; results are the same for every value).  Results are
+ *    deterministic: the same inputs on the same device give the same bits.
+ *    The prefill-sized expert GEMMs cut the items of their last partial wave
+ *    along K by the device's compute-unit count, so their float32 sums (not
+ *    the routing or dispatch) may round differently on a device with another
+ *    count.
  *  - A slot is s = t*k + i (token t, its i-th chosen expert).  Expert ids in
  *    index arrays are global ids in [0, E).
  *  - Formats: activations and the router matrix are MOE_F32 or MOE_BF16;
