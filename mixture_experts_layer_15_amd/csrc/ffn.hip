@@ -476,8 +476,12 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
   const int jmax = max(0, min(per_x, nu - xcd * per_x));  // XCD's slots with a tail unit
   const int nv = jb < vw / kNumXcd ? (vw / kNumXcd - jb + gx - 1) / gx : 0;  // b's workers
   const int n1 = jb < jmax ? (jmax - jb + gx - 1) / gx : 0;  // ... with a tail unit
-  const int it_begin = (int)((long long)n_items * xcd / kNumXcd);
-  const int it_end = (int)((long long)n_items * (xcd + 1) / kNumXcd);
+  // router mode: each tile's K range may be cut into a.ksplit parts, whose
+  // float32 products go to separate planes (the top-k kernels add them in
+  // part order); the plain XCD ranges then run over (part, item)
+  const int rks = kRouter ? max(a.ksplit, 1) : 1;
+  const int it_begin = (int)((long long)n_items * rks * xcd / kNumXcd);
+  const int it_end = (int)((long long)n_items * rks * (xcd + 1) / kNumXcd);
   // Without a split (tp.s == 1) the items keep the plain XCD ranges: the
   // last partial wave then runs next to the items of the same M tiles on each
   // XCD (measured 2-4 % faster than dealing the tail items out separately).
@@ -486,7 +490,12 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
                             : max(0, (it_end - it_begin - slot + per_xcd - 1) / per_xcd);
   auto unit = [&](int k) -> Unit {
     if (!split) {
-      return Unit{it_begin + slot + k * per_xcd, 0, nK, -1};
+      const int idx = it_begin + slot + k * per_xcd;
+      if (kRouter && rks > 1) {
+        const int q = idx / n_items;  // part q of every item, then part q + 1
+        return Unit{idx % n_items, part_begin(q, rks, nK, 1), part_begin(q + 1, rks, nK, 1), q};
+      }
+      return Unit{idx, 0, nK, -1};
     } else {
       int vi, r;
       if (k < n1 * (fw + 1)) {
@@ -588,7 +597,7 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
   auto set_src = [&](int j, int row0, int row_end, int n0, const int* rows, int k0) {
     j = __builtin_amdgcn_readfirstlane(j);
     if constexpr (kRotK) qrot = __builtin_amdgcn_readfirstlane((j * 3 + n0 / 32) % nK);
-    if constexpr (kTail) qrot = __builtin_amdgcn_readfirstlane(k0);
+    if constexpr (kTail || kRouter) qrot = __builtin_amdgcn_readfirstlane(k0);
     row0 = __builtin_amdgcn_readfirstlane(row0);
     row_end = __builtin_amdgcn_readfirstlane(row_end);
     const uint32_t arow_bytes = (uint32_t)a.K * 2;
@@ -966,7 +975,8 @@ __global__ __launch_bounds__(kWave* WM* WN, kMinBlocks) void grouped_gemm_kernel
       for (int m = 0; m < MB; ++m) {
         const int p = c0 + arow_base + m * 32;
         if (p < ce) {
-          float* orow = a.out_f32 + (long long)p * a.Nout;
+          float* orow =
+              a.out_f32 + ((long long)(U.u > 0 ? U.u : 0) * a.rows + p) * a.Nout;  // part plane
 #pragma unroll
           for (int n = 0; n < NB; ++n) {
             const int col = n0c + wn * NB * 32 + n * 32 + 16 * g;
@@ -1661,27 +1671,47 @@ size_t split_part_bytes(const Shape& s) {
 
 bool use_router_gemm(const Shape& s) { return s.act == kBF16 && s.T >= 1024; }
 
+namespace {
+// Router GEMM tiles: 256 x 256 from kRouterBigFrom tokens (bytes staged per
+// MFMA as in the prefill expert GEMMs), else 32 x 256 (four waves side by
+// side along the experts).  With fewer items than compute units, each tile's
+// K range is cut into parts (at least 8 K stages each) so that about one
+// item runs per compute unit.
+constexpr int kRouterBigFrom = 8192;
+struct RouterGemmPlan {
+  int bm, ks;
+};
+RouterGemmPlan router_gemm_plan(const Shape& s) {
+  const int bm = s.T >= kRouterBigFrom ? 256 : 32;
+  const long long items = (long long)((s.T + bm - 1) / bm) * ((s.E + 255) / 256);
+  const int max_ks = std::max(1, std::min(16, s.d / 64 / 8));
+  int ks = (int)std::max<long long>(1, std::min<long long>(max_ks, 256 / std::max(items, 1LL)));
+  return {bm, ks};
+}
+}  // namespace
+
+int router_gemm_splits(const Shape& s) { return router_gemm_plan(s).ks; }
+
 hipError_t router_gemm(const Shape& s, const void* x, const void* w_router_t, float* prod,
                        hipStream_t st) {
   const LaunchEnv env = launch_env();
+  const RouterGemmPlan rp = router_gemm_plan(s);
   GemmArgs a{};
   a.A = static_cast<const uint16_t*>(x);
   a.a_bytes = (uint32_t)((size_t)s.T * s.d * 2);
   a.k = 1;
   a.W0 = w_router_t;
-  a.out_f32 = prod;
+  a.out_f32 = prod;  // [ks][T][E]
   a.rows = s.T;
   a.K = s.d;
   a.Nout = s.E;
   a.n_tiles_n = (s.E + 255) / 256;
   a.group_m = 1;
-  // 32 x 256 tiles (four waves side by side along the experts); 64-row tiles
-  // once there are enough of them, which halves the router matrix re-reads
-  if (s.T >= 16384)
-    return launch_gemm<2, 1, 2, 4, false, 16, 64, 4, 1, true>(
-        a, (long long)((s.T + 63) / 64) * a.n_tiles_n, env, st);
-  return launch_gemm<1, 1, 2, 4, false, 16, 64, 4, 1, true>(
-      a, (long long)((s.T + 31) / 32) * a.n_tiles_n, env, st);
+  a.ksplit = rp.ks;
+  const long long items = (long long)((s.T + rp.bm - 1) / rp.bm) * a.n_tiles_n * rp.ks;
+  if (rp.bm == 256)
+    return launch_gemm<2, 4, 4, 2, false, 16, 64, 2, 1, true>(a, items, env, st);
+  return launch_gemm<1, 1, 2, 4, false, 16, 64, 4, 1, true>(a, items, env, st);
 }
 
 FfnSchedule ffn_schedule_view(const Shape& s, void* ws) {

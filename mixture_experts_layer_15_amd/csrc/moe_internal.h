@@ -53,7 +53,10 @@ hipError_t route(const Shape& s, const void* x, const void* w_router, const floa
                  void* scratch, hipStream_t st);
 bool use_router_gemm(const Shape& s);
 
-// prod [T][E] = x W_r (float32 accumulation) from the router matrix stored [E][d]
+// prod [ks][T][E] = x W_r (float32 accumulation, K cut into
+// ks = router_gemm_splits(s) parts, one plane each) from the router matrix
+// stored [E][d]
+int router_gemm_splits(const Shape& s);
 hipError_t router_gemm(const Shape& s, const void* x, const void* w_router_t, float* prod,
                        hipStream_t st);
 

@@ -550,7 +550,7 @@ bool direct_router(const Shape& s) { return s.act == kBF16 && s.E <= 32; }
 size_t wt_bytes(const Shape& s) {
   return (gemm_router(s) || direct_router(s)) ? align_up((size_t)s.E * s.d * 2) : 0;
 }
-int splits_of(const Shape& s) { return gemm_router(s) ? 1 : router_splits(s); }
+int splits_of(const Shape& s) { return gemm_router(s) ? router_gemm_splits(s) : router_splits(s); }
 }  // namespace
 
 size_t route_ws_bytes(const Shape& s) {

@@ -194,6 +194,16 @@ SMALL = {
     "bf16_router_gemm_odd_E": synth.WORKLOADS["prefill"].replace(
         name="bf16_T1030_d256_E130_k3_F128_zipf", T=1030, d=256, E=130, num_local=130, k=3,
         F=128, seed=32),
+    # the router GEMM with its K range cut into parts (35 tiles of 32 tokens,
+    # 4 parts), summed in part order by the top-k kernel
+    "bf16_router_gemm_ksplit": synth.WORKLOADS["prefill"].replace(
+        name="bf16_T1100_d2048_E200_k6_F128_zipf", T=1100, d=2048, E=200, num_local=200, k=6,
+        F=128, seed=78),
+    # many tokens: the router GEMM on 256 x 256 tiles, ragged last token tile,
+    # E not a multiple of 16, K cut into parts
+    "bf16_router_gemm_big": synth.WORKLOADS["prefill"].replace(
+        name="bf16_T8200_d1024_E170_k4_F128_zipf", T=8200, d=1024, E=170, num_local=170, k=4,
+        F=128, seed=79),
     # MXFP4 weights: decode tiles (ragged N tiles of 128 features), and the
     # 128 x 512 tiles on an expert-parallel block with a half-filled N tile
     "mxfp4_decode_tiles": synth.WORKLOADS["decode_mxfp4"].replace(
