@@ -518,6 +518,47 @@ def test_all_equal_logits_pick_the_lowest_experts():
     assert torch.allclose(gpu["topk_w"], torch.full((64, 5), 0.2))
 
 
+# Every token routed to the same k experts (planted logits, margin 10 over
+# noise of 0.1), at sizes that select the prefill-sized tile plans: one or two
+# experts then hold every slot (many M tiles of one expert, the others empty),
+# the gate/up tail items are cut along K (d = 1024), and on an expert-parallel
+# rank either two of the hot experts are local or none is (no local slot at
+# all: both GEMMs get no item and every output row is 0).
+HOT = {
+    "bf16_wide_hot2": (synth.WORKLOADS["prefill"].replace(
+        name="hot_bf16_T1500_d1024_E16_k2_F256", T=1500, d=1024, E=16, num_local=16, k=2, F=256,
+        bias=(), seed=111), [3, 11]),
+    "bf16_big_hot1": (synth.WORKLOADS["mixtral"].replace(
+        name="hot_bf16_T2100_d512_E4_k1_F384", T=2100, d=512, E=4, num_local=4, k=1, F=384,
+        bias=(), seed=112), [2]),
+    "fp8_rank_hot": (synth.WORKLOADS["dsv3_rank"].replace(
+        name="hot_fp8_T2000_d1024_E16_local0-7_k4_F384", T=2000, d=1024, E=16, num_local=8,
+        expert_begin=0, k=4, F=384, bias=(), seed=113), [1, 5, 9, 13]),
+    "fp8_rank_none_local": (synth.WORKLOADS["dsv3_rank"].replace(
+        name="hot_fp8_T2000_d512_E16_local0-7_k4_F384_nonlocal", T=2000, d=512, E=16,
+        num_local=8, expert_begin=0, k=4, F=384, bias=(), seed=114), [8, 9, 10, 11]),
+    "mxfp4_hot": (synth.WORKLOADS["decode_mxfp4"].replace(
+        name="hot_mxfp4_T2000_d1024_E16_k4_F384", T=2000, d=1024, E=16, num_local=16, k=4,
+        F=384, bias=(), seed=115, regime="prefill"), [0, 6, 7, 15]),
+}
+
+
+@pytest.mark.parametrize("case", list(HOT))
+def test_all_slots_on_the_same_experts(case):
+    wl, hot = HOT[case]
+    pr = synth.make_problem(wl)
+    g = torch.Generator().manual_seed(wl.seed + 1)
+    L = 0.1 * torch.randn((wl.T, wl.E), generator=g)
+    L[:, hot] += 10.0
+    gpu = forward(pr, logits_in=L)
+    assert torch.equal(torch.sort(gpu["topk_idx"], dim=1).values,
+                       torch.tensor(hot, dtype=torch.int32).repeat(wl.T, 1))
+    ref, _ = check(pr, gpu, check_logits=False)
+    local = [e for e in hot if wl.expert_begin <= e < wl.expert_begin + wl.num_local]
+    assert int(ref["offsets"][-1]) == wl.T * len(local)
+    if not local:
+        assert torch.count_nonzero(gpu["out"]) == 0
+
 def test_tokens_without_local_slot_get_zero_and_ranks_sum_to_the_layer():
     base = synth.WORKLOADS["dsv3_rank"].replace(name="ep4", T=128, d=256, E=16, k=2, F=256,
                                                 expert_begin=0, num_local=16, weight="bf16")
