@@ -1085,15 +1085,20 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs a, int nK, in
 // into LDS K-major ([k][row], so the 32 lanes that share a K index read 32
 // consecutive words: no bank conflicts), then each wave runs 16
 // v_mfma_f32_32x32x2_f32 per block (float32 products and sums throughout).
+// The float32 problems are small, so a stage's time is the latency of its
+// loads: each thread holds the next kF32Ahead stages' loads in registers, and
+// the LDS stages alternate between two buffers, one barrier per stage.
 constexpr int kF32BM = 32;
 constexpr int kF32BN = 128;
 constexpr int kF32BK = 32;
+constexpr int kF32Ahead = 2;
 
 template <bool kGateUp>
 __global__ __launch_bounds__(256) void grouped_f32_kernel(GemmArgs a) {
   constexpr int kMats = kGateUp ? 2 : 1;
-  __shared__ float As[kF32BK][kF32BM];
-  __shared__ float Bs[kMats][kF32BK][kF32BN];
+  constexpr int kWv = kF32BN / 32;  // weight float4 loads per thread and matrix
+  __shared__ float As[2][kF32BK][kF32BM];
+  __shared__ float Bs[2][kMats][kF32BK][kF32BN];
   const int n_items = *a.ntiles * a.n_tiles_n;
   const float* A = reinterpret_cast<const float*>(a.A);
   const float* W0 = static_cast<const float*>(a.W0);
@@ -1102,6 +1107,7 @@ __global__ __launch_bounds__(256) void grouped_f32_kernel(GemmArgs a) {
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int l = lane_id();
+  const int nK = a.K / kF32BK;
   // staging: thread tid copies float4 chunk (tid % 8) of K of activation row
   // tid / 8, and of weight rows tid / 8 + 32 i
   const int sr = tid / 8, sk = (tid % 8) * 4;
@@ -1112,38 +1118,67 @@ __global__ __launch_bounds__(256) void grouped_f32_kernel(GemmArgs a) {
     const int p_st = min(row0 + sr, row_end - 1);
     const long long arow = kGateUp ? (long long)(a.sorted_slot[p_st] / a.k) : (long long)p_st;
     const float* asrc = A + arow * a.K + sk;
+    const float* wsrc[kMats][kWv];
+#pragma unroll
+    for (int m = 0; m < kMats; ++m)
+#pragma unroll
+      for (int i = 0; i < kWv; ++i)
+        wsrc[m][i] = (m == 0 ? W0 : W1) +
+                     ((long long)j * a.Nout + min(n0 + sr + 32 * i, a.Nout - 1)) * a.K + sk;
+    // the loads of stage s sit in register set s % 2, which is also its LDS
+    // buffer (register and LDS buffers indexed by compile-time constants)
+    static_assert(kF32Ahead == 2, "two register sets, two LDS buffers");
+    f32x4_t ra[2];
+    f32x4_t rw[2][kMats][kWv];
+    auto load = [&](int s, auto bc) {
+      constexpr int b = decltype(bc)::value;
+      ra[b] = *reinterpret_cast<const f32x4_t*>(asrc + s * kF32BK);
+#pragma unroll
+      for (int m = 0; m < kMats; ++m)
+#pragma unroll
+        for (int i = 0; i < kWv; ++i)
+          rw[b][m][i] = *reinterpret_cast<const f32x4_t*>(wsrc[m][i] + s * kF32BK);
+    };
     f32x16_t acc[kMats];
 #pragma unroll
     for (int m = 0; m < kMats; ++m) acc[m] = f32x16_t{};
-    for (int k0 = 0; k0 < a.K; k0 += kF32BK) {
-      const f32x4_t av = *reinterpret_cast<const f32x4_t*>(asrc + k0);
+    // stage s: into LDS buffer s % 2 (its last readers, the MFMAs of stage
+    // s - 2, are behind the barrier of stage s - 1), barrier, the loads of
+    // stage s + 2 into the freed registers, then the MFMAs
+    auto stage = [&](int s, auto bc) {
+      constexpr int b = decltype(bc)::value;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) As[sk + q][sr] = av[q];
+      for (int q = 0; q < 4; ++q) As[b][sk + q][sr] = ra[b][q];
 #pragma unroll
-      for (int m = 0; m < kMats; ++m) {
-        const float* W = m == 0 ? W0 : W1;
+      for (int m = 0; m < kMats; ++m)
 #pragma unroll
-        for (int i = 0; i < kF32BN / 32; ++i) {
-          const int col = min(n0 + sr + 32 * i, a.Nout - 1);
-          const f32x4_t wv = *reinterpret_cast<const f32x4_t*>(
-              W + ((long long)j * a.Nout + col) * a.K + k0 + sk);
+        for (int i = 0; i < kWv; ++i)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) Bs[m][sk + q][sr + 32 * i] = wv[q];
-        }
-      }
+          for (int q = 0; q < 4; ++q) Bs[b][m][sk + q][sr + 32 * i] = rw[b][m][i][q];
       __syncthreads();
+      if (s + 2 < nK) load(s + 2, bc);
       // v_mfma_f32_32x32x2_f32: lane l gives A[row l % 32][k l / 32] and
       // B[k l / 32][column l % 32]
 #pragma unroll
       for (int kk = 0; kk < kF32BK; kk += 2) {
-        const float av2 = As[kk + l / 32][l % 32];
+        const float av2 = As[b][kk + l / 32][l % 32];
 #pragma unroll
         for (int m = 0; m < kMats; ++m)
-          acc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(av2, Bs[m][kk + l / 32][wave * 32 + l % 32],
-                                                        acc[m], 0, 0, 0);
+          acc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+              av2, Bs[b][m][kk + l / 32][wave * 32 + l % 32], acc[m], 0, 0, 0);
       }
-      __syncthreads();
+    };
+    constexpr std::integral_constant<int, 0> kB0{};
+    constexpr std::integral_constant<int, 1> kB1{};
+    load(0, kB0);
+    if (nK > 1) load(1, kB1);
+    for (int s = 0; s < nK; s += 2) {
+      stage(s, kB0);
+      if (s + 1 < nK) stage(s + 1, kB1);
     }
+    // the next item's first stage goes to LDS buffer 0, last read by this
+    // item's stage nK - 2
+    __syncthreads();
     // result block [token row][column]: lane l holds column l % 32, register
     // r row 8 (r / 4) + 4 (l / 32) + r % 4
     const int col = n0 + wave * 32 + l % 32;
@@ -1811,12 +1846,15 @@ hipError_t expert_ffn(const Shape& s, const void* x, const int32_t* sorted_slot,
   if (s.weight == kF32) {
     gu.n_tiles_n = (s.F + kF32BN - 1) / kF32BN;
     dn.n_tiles_n = (s.d + kF32BN - 1) / kF32BN;
-    const int grid = 4 * env.num_cu;
-    hipLaunchKernelGGL(grouped_f32_kernel<true>, dim3(grid), dim3(256), 0, st, gu);
+    // a workgroup per possible item, at most four per CU (the items loop)
+    auto grid = [&](int ntn) {
+      return (unsigned)std::max<long long>(1, std::min<long long>(4LL * env.num_cu, mt * ntn));
+    };
+    hipLaunchKernelGGL(grouped_f32_kernel<true>, dim3(grid(gu.n_tiles_n)), dim3(256), 0, st, gu);
     e = hipGetLastError();
     if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(grouped_f32_kernel<false>, dim3(grid), dim3(256), 0, st, dn);
+    hipLaunchKernelGGL(grouped_f32_kernel<false>, dim3(grid(dn.n_tiles_n)), dim3(256), 0, st, dn);
     e = hipGetLastError();
     if (e == hipSuccess && ev) e = hipEventRecord(ev[2], st);
     return e;

@@ -260,22 +260,84 @@ __global__ __launch_bounds__(kThreads) void router_partial_direct(PartialArgs a)
   }
 }
 
-// float32 router: each thread forms whole dot products over its K range in order.
+// float32 router on the fp32 matrix cores: workgroup (32-token tile, K
+// split), 128 experts per pass, each wave one 32 x 32 block of
+// v_mfma_f32_32x32x2_f32 (float32 products and sums).  Per 32-deep K stage
+// the x tile and the router rows (read as stored, [d][E], consecutive lanes
+// on consecutive experts) go to LDS K-major; the loads of the next two
+// stages wait in registers and the LDS stages alternate between two
+// buffers, one barrier per stage (the float32 problems are small, so a
+// stage costs the latency of its loads).
+constexpr int kRK = 32;  // K per stage
 __global__ __launch_bounds__(kThreads) void router_partial_f32(PartialArgs a) {
+  __shared__ float As[2][kRK][kBM];
+  __shared__ float Bs[2][kRK][kCC];
   const float* x = static_cast<const float*>(a.x);
   const float* wr = static_cast<const float*>(a.w);
+  const int tid = threadIdx.x;
+  const int w = tid / kWave;
+  const int l = lane_id();
   const int t0 = blockIdx.x * kBM;
   const int kbeg = blockIdx.y * a.k_per_split;
+  const int nK = a.k_per_split / kRK;
   float* out = a.out + (size_t)blockIdx.y * a.T * a.E;
-  for (int o = threadIdx.x; o < kBM * a.E; o += kThreads) {
-    const int r = o / a.E, e = o % a.E;
-    const int t = t0 + r;
-    if (t >= a.T) continue;
-    const float* xr = x + (size_t)t * a.d;
-    float acc = 0.f;
-    for (int c = kbeg; c < kbeg + a.k_per_split; ++c)
-      acc = fmaf(xr[c], wr[(size_t)c * a.E + e], acc);
-    out[(size_t)t * a.E + e] = acc;
+  // x: thread tid stages float4 (tid % 8) of token row tid / 8 (clamped);
+  // W_r: rows tid / 32 + 8 i, experts c0 + tid % 32 + 32 q (0 past E)
+  const int sr = tid / 8, sk = (tid % 8) * 4;
+  const float* xsrc = x + (size_t)min(t0 + sr, a.T - 1) * a.d + kbeg + sk;
+  const int wk = tid / 32, we = tid % 32;
+  f32x4_t ra[2];
+  float rb[2][4][4];
+  for (int c0 = 0; c0 < a.E; c0 += kCC) {
+    auto load = [&](int s, auto bc) {
+      constexpr int b = decltype(bc)::value;
+      ra[b] = *reinterpret_cast<const f32x4_t*>(xsrc + s * kRK);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float* row = wr + (size_t)(kbeg + s * kRK + wk + 8 * i) * a.E;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int e = c0 + we + 32 * q;
+          rb[b][i][q] = e < a.E ? row[e] : 0.0f;
+        }
+      }
+    };
+    f32x16_t acc = f32x16_t{};
+    auto stage = [&](int s, auto bc) {
+      constexpr int b = decltype(bc)::value;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) As[b][sk + q][sr] = ra[b][q];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) Bs[b][wk + 8 * i][we + 32 * q] = rb[b][i][q];
+      __syncthreads();
+      if (s + 2 < nK) load(s + 2, bc);
+      // lane l gives A[token l % 32][k l / 32] and B[k l / 32][expert l % 32]
+#pragma unroll
+      for (int kk = 0; kk < kRK; kk += 2)
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[b][kk + l / 32][l % 32],
+                                                   Bs[b][kk + l / 32][w * 32 + l % 32], acc, 0,
+                                                   0, 0);
+    };
+    constexpr std::integral_constant<int, 0> kB0{};
+    constexpr std::integral_constant<int, 1> kB1{};
+    load(0, kB0);
+    if (nK > 1) load(1, kB1);
+    for (int s = 0; s < nK; s += 2) {
+      stage(s, kB0);
+      if (s + 1 < nK) stage(s + 1, kB1);
+    }
+    // lane l holds expert c0 + 32 w + l % 32, token rows 8 (r / 4) + 4 (l / 32) + r % 4
+    const int e = c0 + w * 32 + l % 32;
+    if (e < a.E) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = t0 + 8 * (r / 4) + 4 * (l / 32) + (r % 4);
+        if (t < a.T) out[(size_t)t * a.E + e] = acc[r];
+      }
+    }
+    __syncthreads();  // the next pass's first stage reuses LDS buffer 0
   }
 }
 

@@ -222,6 +222,11 @@ SMALL = {
     # f32 with more tiles than the tiny workload
     "f32_tiles": synth.WORKLOADS["tiny"].replace(
         name="f32_T300_d256_E8_k3_F384", T=300, d=256, E=8, num_local=8, k=3, F=384, seed=26),
+    # f32 router product over two expert passes (150 experts: the second pass
+    # masked past E) and four K splits
+    "f32_router_E150": synth.WORKLOADS["tiny"].replace(
+        name="f32_T100_d512_E150_k4_F128", T=100, d=512, E=150, num_local=150, k=4, F=128,
+        seed=39),
 }
 
 
